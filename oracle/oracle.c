@@ -1,0 +1,379 @@
+/*
+ * Oracle for the chunked spatio-temporal attention queue step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is a plain, slow, fp64 CPU statement
+ * of what the GPU path must compute.  Only the test suite, the smoke check and
+ * the CPU-baseline leg of the benchmark load it; the product library never
+ * does, and the two share no code, headers or tables.
+ *
+ * What is computed (cited by page title and section):
+ *
+ *  - "双重并行：让AI视频生成突破时长限制" (techwalker write-up of DualParal,
+ *    arXiv:2505.21070), section 二 (FIFO queue and block-wise denoising): the
+ *    video is split into fixed-size,
+ *    non-overlapping temporal chunks that sit in a FIFO queue and are all
+ *    processed in one step, fed from the tail to the head.
+ *  - same page, section 三 (feature cache): while chunk B_{i+1} is processed
+ *    its self-attention K/V are stored, and the next chunk processed (B_i)
+ *    reuses them instead of re-concatenating that chunk; only self-attention
+ *    uses the cache, cross-attention and the FFN stay per chunk.
+ *  - "视频扩散模型：核心技术挑战与前沿进展" (intelliparadigm survey),
+ *    section 2.1, item 2: spatio-temporal attention attends jointly over all
+ *    tokens of all frames in the window, at quadratic cost.
+ *
+ * Reading used here.  Chunk c of the call is the c-th chunk in processing
+ * order; its "predecessor" is chunk c-1 (the chunk processed just before it,
+ * the page's B_{i+1}).  Chunk 0 has no predecessor and so a zero-length cache.
+ * For query row r of chunk c and head h, the key/value set is
+ *     R_c = [predecessor rows 0..L-1 (if c >= 1)] ++ [own rows 0..L-1]
+ * and the output is plain softmax attention over R_c:
+ *     s_j = scale * <q, k_j>,  O = sum_j exp(s_j - max s) v_j / sum_j exp(s_j - max s)
+ * with no mask inside R_c.  The predecessor rows come either from a separate
+ * cache buffer (slot c holds chunk c-1's K then V) or, when no cache buffer is
+ * given, straight from chunk c-1's own K/V.
+ *
+ * Precision.  Every input element is widened exactly to fp64 (bf16 and fp32
+ * both embed exactly); scores, exponentials, sums and the weighted sum are
+ * fp64, the dot product summed in increasing dimension order.  Two passes per
+ * row: all scores first, then the normalised weighted sum.  No tiling, no
+ * running maximum.
+ *
+ * Layouts (row-major, element offsets):
+ *   q, k, v, out      [n_chunks][L][H][D]
+ *   kv_cache          [n_chunks][2][L][H][D]   (slot c: K of c-1, then V of c-1)
+ *   full attention    q/out [batch][Lq][H][D],  k/v batch b at b*kv_batch_stride,
+ *                     each [Lkv][H][D]
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_BF16 = 0, ORACLE_F32 = 1, ORACLE_F64 = 2 };
+enum { ORACLE_SRC_PRED = 0, ORACLE_SRC_OWN = 1 };
+
+/* Widen element i of an array of the given storage type to fp64. */
+static double load_elem(const void *base, int dtype, int64_t i)
+{
+    if (dtype == ORACLE_BF16) {
+        uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)base)[i];
+    return ((const double *)base)[i];
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Size of R_c. */
+int64_t oracle_kv_set_size(int64_t chunk_len, int64_t c)
+{
+    return c >= 1 ? 2 * chunk_len : chunk_len;
+}
+
+/*
+ * The key/value set R_c of chunk c, entry by entry: which source it is read
+ * from (predecessor or own), which chunk's K/V it is, and the token row in that
+ * chunk.  This is the integer map the GPU plan must reproduce bit for bit.
+ */
+int64_t oracle_index_map(int64_t chunk_len, int64_t n_chunks, int64_t c,
+                         int64_t *src, int64_t *chunk, int64_t *row)
+{
+    if (c < 0 || c >= n_chunks || chunk_len < 0)
+        return -1;
+    int64_t j = 0;
+    if (c >= 1) {
+        for (int64_t r = 0; r < chunk_len; ++r, ++j) {
+            src[j] = ORACLE_SRC_PRED;
+            chunk[j] = c - 1;
+            row[j] = r;
+        }
+    }
+    for (int64_t r = 0; r < chunk_len; ++r, ++j) {
+        src[j] = ORACLE_SRC_OWN;
+        chunk[j] = c;
+        row[j] = r;
+    }
+    return j;
+}
+
+/* Element offsets of the K and V row for entry j of R_c, head h, dim 0. */
+static void kv_offsets(int64_t j, int64_t c, int64_t L, int64_t H, int64_t D,
+                       int has_cache, int64_t *k_off, int64_t *v_off,
+                       int *from_cache)
+{
+    int64_t lc = c >= 1 ? L : 0;
+    if (j < lc) {
+        if (has_cache) {
+            /* cache slot c: [2][L][H][D], K first then V */
+            *k_off = ((c * 2 + 0) * L + j) * H * D;
+            *v_off = ((c * 2 + 1) * L + j) * H * D;
+            *from_cache = 1;
+        } else {
+            /* predecessor read in place from chunk c-1 */
+            *k_off = ((c - 1) * L + j) * H * D;
+            *v_off = *k_off;
+            *from_cache = 0;
+        }
+    } else {
+        *k_off = (c * L + (j - lc)) * H * D;
+        *v_off = *k_off;
+        *from_cache = 0;
+    }
+}
+
+/*
+ * Attention of one query row (q_off: element offset of (token, head, 0) in q)
+ * over nk key/value rows whose element offsets are given by the callback data.
+ * Writes the D outputs to out; when probs is non-NULL also writes the nk
+ * softmax weights.  s is scratch of nk doubles.
+ */
+typedef struct {
+    const void *k, *v, *ck;
+    int64_t c, L, H, D, h;
+    int has_cache;
+    /* full attention */
+    int64_t kv_base;
+    int full;
+} kv_source;
+
+static void row_kv(const kv_source *src, int64_t j, const void **kb, int64_t *ko,
+                   const void **vb, int64_t *vo)
+{
+    if (src->full) {
+        *kb = src->k;
+        *vb = src->v;
+        *ko = src->kv_base + (j * src->H + src->h) * src->D;
+        *vo = *ko;
+        return;
+    }
+    int64_t k_off, v_off;
+    int from_cache;
+    kv_offsets(j, src->c, src->L, src->H, src->D, src->has_cache, &k_off, &v_off,
+               &from_cache);
+    k_off += src->h * src->D;
+    v_off += src->h * src->D;
+    if (from_cache) {
+        *kb = src->ck;
+        *vb = src->ck;
+    } else {
+        *kb = src->k;
+        *vb = src->v;
+    }
+    *ko = k_off;
+    *vo = v_off;
+}
+
+static void attend_row(int dtype, const void *q, int64_t q_off, const kv_source *src,
+                       int64_t nk, double scale, double *s, double *out, double *probs)
+{
+    const int64_t D = src->D;
+    /* pass 1: scores */
+    for (int64_t j = 0; j < nk; ++j) {
+        const void *kb, *vb;
+        int64_t ko, vo;
+        row_kv(src, j, &kb, &ko, &vb, &vo);
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            acc += load_elem(q, dtype, q_off + d) * load_elem(kb, dtype, ko + d);
+        s[j] = scale * acc;
+    }
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nk; ++j)
+        if (s[j] > m)
+            m = s[j];
+    double z = 0.0;
+    for (int64_t j = 0; j < nk; ++j) {
+        s[j] = exp(s[j] - m);
+        z += s[j];
+    }
+    /* pass 2: normalised weighted sum of V */
+    for (int64_t d = 0; d < D; ++d)
+        out[d] = 0.0;
+    for (int64_t j = 0; j < nk; ++j) {
+        const void *kb, *vb;
+        int64_t ko, vo;
+        row_kv(src, j, &kb, &ko, &vb, &vo);
+        double w = s[j] / z;
+        if (probs)
+            probs[j] = w;
+        for (int64_t d = 0; d < D; ++d)
+            out[d] += w * load_elem(vb, dtype, vo + d);
+    }
+}
+
+static kv_source queue_source(const void *k, const void *v, const void *kv_cache,
+                              int64_t c, int64_t h, int64_t L, int64_t H, int64_t D)
+{
+    kv_source src;
+    memset(&src, 0, sizeof src);
+    src.k = k;
+    src.v = v;
+    src.ck = kv_cache;
+    src.c = c;
+    src.h = h;
+    src.L = L;
+    src.H = H;
+    src.D = D;
+    src.has_cache = kv_cache != NULL;
+    return src;
+}
+
+/*
+ * Queue step over selected rows.  rows holds n_rows triples (chunk, head, row);
+ * out receives n_rows x D doubles.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_queue_rows(int dtype, const void *q, const void *k, const void *v,
+                      const void *kv_cache, int64_t L, int64_t n_chunks, int64_t H,
+                      int64_t D, double scale, const int64_t *rows, int64_t n_rows,
+                      double *out)
+{
+    if (L <= 0 || n_chunks <= 0 || H <= 0 || D <= 0)
+        return -1;
+    for (int64_t i = 0; i < n_rows; ++i) {
+        int64_t c = rows[3 * i], h = rows[3 * i + 1], r = rows[3 * i + 2];
+        if (c < 0 || c >= n_chunks || h < 0 || h >= H || r < 0 || r >= L)
+            return -1;
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * 2 * L);
+        if (!s) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t i = 0; i < n_rows; ++i) {
+                int64_t c = rows[3 * i], h = rows[3 * i + 1], r = rows[3 * i + 2];
+                kv_source src = queue_source(k, v, kv_cache, c, h, L, H, D);
+                int64_t q_off = ((c * L + r) * H + h) * D;
+                attend_row(dtype, q, q_off, &src, oracle_kv_set_size(L, c), scale, s,
+                           out + i * D, NULL);
+            }
+            free(s);
+        }
+    }
+    return bad ? -2 : 0;
+}
+
+/* Whole queue step: out is [n_chunks][L][H][D] doubles. */
+int oracle_queue_step(int dtype, const void *q, const void *k, const void *v,
+                      const void *kv_cache, int64_t L, int64_t n_chunks, int64_t H,
+                      int64_t D, double scale, double *out)
+{
+    if (L <= 0 || n_chunks <= 0 || H <= 0 || D <= 0)
+        return -1;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * 2 * L);
+        if (!s) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for collapse(3) schedule(dynamic, 4)
+            for (int64_t c = 0; c < n_chunks; ++c)
+                for (int64_t r = 0; r < L; ++r)
+                    for (int64_t h = 0; h < H; ++h) {
+                        kv_source src = queue_source(k, v, kv_cache, c, h, L, H, D);
+                        int64_t off = ((c * L + r) * H + h) * D;
+                        attend_row(dtype, q, off, &src, oracle_kv_set_size(L, c), scale,
+                                   s, out + off, NULL);
+                    }
+            free(s);
+        }
+    }
+    return bad ? -2 : 0;
+}
+
+/* Softmax weights of one query row over R_c, in index-map order. */
+int oracle_queue_probs(int dtype, const void *q, const void *k, const void *v,
+                       const void *kv_cache, int64_t L, int64_t n_chunks, int64_t H,
+                       int64_t D, double scale, int64_t c, int64_t h, int64_t r,
+                       double *probs, double *out_row)
+{
+    if (L <= 0 || c < 0 || c >= n_chunks || h < 0 || h >= H || r < 0 || r >= L)
+        return -1;
+    int64_t nk = oracle_kv_set_size(L, c);
+    double *s = (double *)malloc(sizeof(double) * nk);
+    if (!s)
+        return -2;
+    kv_source src = queue_source(k, v, kv_cache, c, h, L, H, D);
+    attend_row(dtype, q, ((c * L + r) * H + h) * D, &src, nk, scale, s, out_row, probs);
+    free(s);
+    return 0;
+}
+
+/*
+ * Full (non-chunked) attention, also used for per-chunk cross-attention to a
+ * shared text K/V (kv_batch_stride = 0).  rows: n_rows triples (batch, head,
+ * query row); out: n_rows x D.  Pass rows = NULL to compute every row, in
+ * which case out is [batch][Lq][H][D].
+ */
+int oracle_full_rows(int dtype, const void *q, const void *k, const void *v,
+                     int64_t batch, int64_t lq, int64_t lkv, int64_t kv_batch_stride,
+                     int64_t H, int64_t D, double scale, const int64_t *rows,
+                     int64_t n_rows, double *out)
+{
+    if (batch <= 0 || lq <= 0 || lkv <= 0 || H <= 0 || D <= 0 || kv_batch_stride < 0)
+        return -1;
+    int all = rows == NULL;
+    int64_t total = all ? batch * lq * H : n_rows;
+    if (!all)
+        for (int64_t i = 0; i < n_rows; ++i) {
+            int64_t b = rows[3 * i], h = rows[3 * i + 1], r = rows[3 * i + 2];
+            if (b < 0 || b >= batch || h < 0 || h >= H || r < 0 || r >= lq)
+                return -1;
+        }
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * lkv);
+        if (!s) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t i = 0; i < total; ++i) {
+                int64_t b, h, r;
+                if (all) {
+                    h = i % H;
+                    r = (i / H) % lq;
+                    b = i / (H * lq);
+                } else {
+                    b = rows[3 * i];
+                    h = rows[3 * i + 1];
+                    r = rows[3 * i + 2];
+                }
+                kv_source src;
+                memset(&src, 0, sizeof src);
+                src.full = 1;
+                src.k = k;
+                src.v = v;
+                src.H = H;
+                src.D = D;
+                src.h = h;
+                src.kv_base = b * kv_batch_stride;
+                int64_t q_off = ((b * lq + r) * H + h) * D;
+                double *dst = all ? out + q_off : out + i * D;
+                attend_row(dtype, q, q_off, &src, lkv, scale, s, dst, NULL);
+            }
+            free(s);
+        }
+    }
+    return bad ? -2 : 0;
+}

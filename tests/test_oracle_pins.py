@@ -1,0 +1,339 @@
+"""Pins for the fp64 CPU oracle, against things other than itself.
+
+Each test checks the oracle against what the pages and the mathematics fix:
+hand-derived closed forms (tests/golden), invariants of softmax attention, a
+brute-force re-formulation (attention over the explicitly concatenated
+sequence with a block-band mask, which is what the page's K/V cache replaces,
+DualParal write-up section 三), torch's own scaled-dot-product attention, and
+special cases that reduce to textbook attention.  The pins are chosen so that
+plausible slips in the oracle (dropped cache rows, a wrong predecessor index,
+a missing scale, V read from K, heads mixed) each fail at least one of them;
+tests/test_oracle_mutations.py plants such slips and checks exactly that.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+def rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def band_masked_attention(q, k, v, scale):
+    """Attention over the concatenated sequence of all chunks, with the block
+    band mask: a query in chunk c sees keys of chunks c-1 and c only.
+
+    This is the explicit-concatenation form that the page's cache avoids; it is
+    written independently of the oracle (one dense score matrix per head).
+    """
+    n, L, H, D = q.shape
+    S = n * L
+    qs = q.reshape(S, H, D)
+    ks = k.reshape(S, H, D)
+    vs = v.reshape(S, H, D)
+    chunk_of = np.arange(S) // L
+    allowed = (chunk_of[None, :] == chunk_of[:, None]) | (chunk_of[None, :] == chunk_of[:, None] - 1)
+    out = np.empty((S, H, D))
+    for h in range(H):
+        s = scale * qs[:, h, :] @ ks[:, h, :].T
+        s = np.where(allowed, s, -np.inf)
+        s = s - s.max(axis=1, keepdims=True)
+        w = np.exp(s)
+        w /= w.sum(axis=1, keepdims=True)
+        out[:, h, :] = w @ vs[:, h, :]
+    return out.reshape(n, L, H, D)
+
+
+def make_cache(k, v):
+    n = k.shape[0]
+    cache = np.full((n, 2) + k.shape[1:], np.nan)
+    cache[1:, 0] = k[:-1]
+    cache[1:, 1] = v[:-1]
+    return cache
+
+
+# --------------------------------------------------------------------------
+# golden closed forms
+
+
+def _golden_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_golden_closed_forms(case):
+    q = np.array(case["q"], np.float64)
+    k = np.array(case["k"], np.float64)
+    v = np.array(case["v"], np.float64)
+    cache = None if case["cache"] is None else np.array(case["cache"], np.float64)
+    exp = np.array(case["expected"], np.float64)
+    got = oracle.queue_step(q, k, v, cache, scale=case["scale"])
+    assert got.shape == exp.shape
+    np.testing.assert_allclose(got, exp, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# (a) softmax weights of every row sum to one, and are the closed form
+
+
+@pytest.mark.parametrize("c", [0, 1, 3])
+def test_probs_sum_to_one(c):
+    n, L, H, D = 4, 9, 2, 8
+    q, k, v = rand((n, L, H, D), 1), rand((n, L, H, D), 2), rand((n, L, H, D), 3)
+    for h in range(H):
+        for r in (0, 4, L - 1):
+            p, _ = oracle.queue_probs(q, k, v, None, c, h, r)
+            assert p.shape == (L if c == 0 else 2 * L,)
+            assert np.all(p > 0)
+            assert abs(p.sum() - 1.0) <= 1e-12
+
+
+def test_probs_match_closed_form_weights():
+    # two keys with score gap ln 3 -> weights exactly (1/4, 3/4)
+    q = np.zeros((2, 1, 1, 1))
+    k = np.zeros((2, 1, 1, 1))
+    v = np.zeros((2, 1, 1, 1))
+    q[1, 0, 0, 0] = 1.0
+    k[1, 0, 0, 0] = math.log(3.0)
+    p, _ = oracle.queue_probs(q, k, v, None, 1, 0, 0, scale=1.0)
+    np.testing.assert_allclose(p, [0.25, 0.75], rtol=0, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# (b) constant V is returned exactly
+
+
+@pytest.mark.parametrize("with_cache", [False, True])
+def test_constant_v_returned(with_cache):
+    n, L, H, D = 3, 7, 2, 5
+    q, k = rand((n, L, H, D), 4), rand((n, L, H, D), 5)
+    cvec = rand((1, 1, H, D), 6)
+    v = np.broadcast_to(cvec, (n, L, H, D)).copy()
+    cache = make_cache(k, v) if with_cache else None
+    got = oracle.queue_step(q, k, v, cache)
+    np.testing.assert_allclose(got, np.broadcast_to(cvec, got.shape), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# (c) cache form == explicit concatenation with a block-band mask
+
+
+@pytest.mark.parametrize("shape", [(4, 16, 2, 8), (3, 5, 3, 4), (1, 6, 1, 3), (5, 1, 2, 2)])
+@pytest.mark.parametrize("with_cache", [False, True])
+def test_chunked_equals_band_masked_concatenation(shape, with_cache):
+    n, L, H, D = shape
+    q, k, v = rand(shape, 7), rand(shape, 8), rand(shape, 9)
+    scale = 0.37
+    cache = make_cache(k, v) if with_cache else None
+    got = oracle.queue_step(q, k, v, cache, scale=scale)
+    ref = band_masked_attention(q, k, v, scale)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_chunked_equals_torch_sdpa_with_band_mask():
+    n, L, H, D = 4, 12, 3, 16
+    q, k, v = rand((n, L, H, D), 10), rand((n, L, H, D), 11), rand((n, L, H, D), 12)
+    got = oracle.queue_step(q, k, v, None)
+    S = n * L
+    tq = torch.from_numpy(q.reshape(S, H, D)).permute(1, 0, 2).unsqueeze(0)
+    tk = torch.from_numpy(k.reshape(S, H, D)).permute(1, 0, 2).unsqueeze(0)
+    tv = torch.from_numpy(v.reshape(S, H, D)).permute(1, 0, 2).unsqueeze(0)
+    ch = torch.arange(S) // L
+    mask = (ch[None, :] == ch[:, None]) | (ch[None, :] == ch[:, None] - 1)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask,
+                                                           scale=D ** -0.5)
+    ref = ref.squeeze(0).permute(1, 0, 2).reshape(n, L, H, D).numpy()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_cache_mode_equals_alias_mode():
+    shape = (5, 11, 2, 8)
+    q, k, v = rand(shape, 13), rand(shape, 14), rand(shape, 15)
+    a = oracle.queue_step(q, k, v, None)
+    b = oracle.queue_step(q, k, v, make_cache(k, v))
+    np.testing.assert_array_equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# (d) joint permutation of key/value rows (across the cache/own boundary)
+
+
+def test_joint_kv_permutation_invariance():
+    n, L, H, D = 3, 10, 2, 6
+    q, k, v = rand((n, L, H, D), 16), rand((n, L, H, D), 17), rand((n, L, H, D), 18)
+    cache = make_cache(k, v)
+    base = oracle.queue_step(q, k, v, cache)
+    c = 1
+    # R_c as one 2L-row array, permuted jointly for K and V, then split back
+    kc = np.concatenate([cache[c, 0], k[c]], axis=0)
+    vc = np.concatenate([cache[c, 1], v[c]], axis=0)
+    perm = np.random.default_rng(19).permutation(2 * L)
+    assert np.any(perm[:L] >= L)  # the permutation crosses the cache/own boundary
+    k2, v2, cache2 = k.copy(), v.copy(), cache.copy()
+    cache2[c, 0], k2[c] = kc[perm][:L], kc[perm][L:]
+    cache2[c, 1], v2[c] = vc[perm][:L], vc[perm][L:]
+    # chunk c+1 reads its predecessor from cache slot c+1, which is unchanged
+    got = oracle.queue_step(q, k2, v2, cache2)
+    np.testing.assert_allclose(got[c], base[c], rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(got[c + 1], base[c + 1])
+
+
+def test_query_permutation_permutes_output():
+    n, L, H, D = 2, 9, 2, 4
+    q, k, v = rand((n, L, H, D), 20), rand((n, L, H, D), 21), rand((n, L, H, D), 22)
+    base = oracle.queue_step(q, k, v, None)
+    perm = np.random.default_rng(23).permutation(L)
+    q2 = q.copy()
+    q2[1] = q[1][perm]
+    got = oracle.queue_step(q2, k, v, None)
+    np.testing.assert_allclose(got[1], base[1][perm], rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# reductions to textbook attention and closed forms
+
+
+def _sdpa(q, k, v, scale):
+    """torch fp64 attention for [B][L][H][D] arrays."""
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def test_chunk0_is_plain_attention_on_itself():
+    shape = (3, 14, 2, 8)
+    q, k, v = rand(shape, 24), rand(shape, 25), rand(shape, 26)
+    got = oracle.queue_step(q, k, v, None)
+    ref = _sdpa(q[:1], k[:1], v[:1], 8 ** -0.5)
+    np.testing.assert_allclose(got[:1], ref, rtol=0, atol=1e-12)
+
+
+def test_single_chunk_equals_full():
+    shape = (1, 17, 3, 8)
+    q, k, v = rand(shape, 27), rand(shape, 28), rand(shape, 29)
+    a = oracle.queue_step(q, k, v, None)
+    b = oracle.full(q, k, v)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+def test_full_matches_torch_sdpa_and_shared_kv():
+    q = rand((3, 10, 2, 8), 30)
+    kt, vt = rand((1, 7, 2, 8), 31), rand((1, 7, 2, 8), 32)
+    got = oracle.full(q, kt, vt, scale=0.3)
+    ref = _sdpa(q, np.broadcast_to(kt, (3, 7, 2, 8)).copy(),
+                np.broadcast_to(vt, (3, 7, 2, 8)).copy(), 0.3)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+    # per-batch K/V
+    kb, vb = rand((3, 7, 2, 8), 33), rand((3, 7, 2, 8), 34)
+    np.testing.assert_allclose(oracle.full(q, kb, vb), _sdpa(q, kb, vb, 8 ** -0.5),
+                               rtol=0, atol=1e-12)
+
+
+def test_full_rows_match_full():
+    q, k, v = rand((2, 9, 2, 4), 35), rand((2, 5, 2, 4), 36), rand((2, 5, 2, 4), 37)
+    allr = oracle.full(q, k, v)
+    rows = np.array([[0, 0, 0], [1, 1, 8], [1, 0, 3]])
+    got = oracle.full_rows(q, k, v, rows)
+    for i, (b, h, r) in enumerate(rows):
+        np.testing.assert_array_equal(got[i], allr[b, r, h])
+
+
+@pytest.mark.parametrize("mode", ["zero_q", "zero_scale"])
+def test_uniform_mean_when_scores_vanish(mode):
+    n, L, H, D = 3, 4, 2, 3
+    q, k = rand((n, L, H, D), 38), rand((n, L, H, D), 39)
+    v = np.random.default_rng(40).integers(-8, 9, (n, L, H, D)).astype(np.float64)
+    scale = 0.5
+    if mode == "zero_q":
+        q[:] = 0.0
+    else:
+        scale = 0.0
+    got = oracle.queue_step(q, k, v, None, scale=scale)
+    for c in range(n):
+        lo = max(c - 1, 0)
+        mean = v[lo:c + 1].reshape(-1, H, D).mean(axis=0)
+        np.testing.assert_allclose(got[c], np.broadcast_to(mean, (L, H, D)), rtol=0, atol=1e-13)
+
+
+def test_single_key_returns_its_value():
+    q, k, v = rand((1, 1, 2, 4), 41), rand((1, 1, 2, 4), 42), rand((1, 1, 2, 4), 43)
+    np.testing.assert_allclose(oracle.queue_step(q, k, v, None), v, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("j", [0, 5, 8, 13])
+def test_dominant_key_selects_its_value(j):
+    n, L, H, D = 2, 8, 1, 4
+    q, k, v = rand((n, L, H, D), 44), 0.01 * rand((n, L, H, D), 45), rand((n, L, H, D), 46)
+    qh = q[1, 3, 0] / np.linalg.norm(q[1, 3, 0])
+    # key j of R_1: j < L is the predecessor's (chunk 0) row j, else own row j-L
+    src_c, src_r = (0, j) if j < L else (1, j - L)
+    k[src_c, src_r, 0] = 200.0 * qh
+    got = oracle.queue_step(q, k, v, None, scale=1.0)
+    np.testing.assert_allclose(got[1, 3, 0], v[src_c, src_r, 0], rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# storage types: bf16 and fp32 inputs are widened exactly
+
+
+def test_bf16_and_f32_inputs_widen_exactly():
+    shape = (3, 6, 2, 8)
+    tq = torch.from_numpy(rand(shape, 47)).to(torch.bfloat16)
+    tk = torch.from_numpy(rand(shape, 48)).to(torch.bfloat16)
+    tv = torch.from_numpy(rand(shape, 49)).to(torch.bfloat16)
+    via_bf16 = oracle.queue_step(tq, tk, tv, None)
+    via_f64 = oracle.queue_step(tq.double().numpy(), tk.double().numpy(), tv.double().numpy(),
+                                None)
+    np.testing.assert_array_equal(via_bf16, via_f64)
+    via_f32 = oracle.queue_step(tq.float(), tk.float(), tv.float(), None)
+    np.testing.assert_array_equal(via_f32, via_f64)
+
+
+# --------------------------------------------------------------------------
+# integer index map == brute-force enumeration of the band mask
+
+
+@pytest.mark.parametrize("L,n", [(1, 1), (3, 4), (7, 2), (128, 4)])
+def test_index_map_matches_band_enumeration(L, n):
+    for c in range(n):
+        src, ch, row = oracle.index_map(L, n, c)
+        expect = []
+        for cc in range(n):          # every key token of the concatenated sequence
+            for r in range(L):
+                if cc == c - 1:
+                    expect.append((oracle.SRC_PRED, cc, r))
+                elif cc == c:
+                    expect.append((oracle.SRC_OWN, cc, r))
+        got = list(zip(src.tolist(), ch.tolist(), row.tolist()))
+        assert got == expect
+
+
+def test_queue_rows_match_queue_step():
+    shape = (4, 13, 3, 8)
+    q, k, v = rand(shape, 50), rand(shape, 51), rand(shape, 52)
+    cache = make_cache(k, v)
+    allr = oracle.queue_step(q, k, v, cache)
+    rows = np.array([[0, 0, 0], [3, 2, 12], [1, 1, 6], [2, 0, 0]])
+    got = oracle.queue_rows(q, k, v, cache, rows)
+    for i, (c, h, r) in enumerate(rows):
+        np.testing.assert_array_equal(got[i], allr[c, r, h])
+
+
+def test_cache_slot0_is_never_read():
+    shape = (3, 5, 2, 4)
+    q, k, v = rand(shape, 53), rand(shape, 54), rand(shape, 55)
+    cache = make_cache(k, v)          # slot 0 is NaN
+    assert np.isnan(cache[0]).all()
+    got = oracle.queue_step(q, k, v, cache)
+    assert np.isfinite(got).all()

@@ -1,0 +1,279 @@
+"""Benchmark of the chunk-attention queue step on one MI355X.
+
+One step = one queue step of the timed workload (every chunk's attention over
+[predecessor K/V cache ; own K/V], all chunks x heads x query tiles in one
+launch; for a workload with text tokens also the per-chunk cross-attention).
+Inputs are seeded synthetic tensors already resident in HBM; the timed region
+covers exactly `--steps` steps between a barrier and a device synchronisation.
+
+Prints one JSON line with the throughput (exact FLOPs / time), queue-steps/s,
+the roofline of the dominant kernel (HIP events on the stream the kernel runs
+on) and, on rank 0, the CPU oracle timed on a bounded sample of the same
+workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 256 * 4096 * 2.4e9 / 1e12  # 256 CUs x 4096 FLOP/clk x 2.4 GHz = 2516.6
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "chunked_spatio_temporal_amd", "csrc", f)
+                  for f in ("attn_kernel.h", "plan.h", "chunkattn_api.hip")]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: the 40-head queue)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the queue step shards by head or by chunk range across GPUs, see DESIGN.md)",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from chunked_spatio_temporal_amd import chunkattn as ca
+    from chunked_spatio_temporal_amd import configs, synth
+
+    name = args.workload or configs.BENCH_WORKLOAD
+    w = configs.WORKLOADS[name]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    ca.load_library()
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    t0 = time.time()
+    if w.kind == "queue":
+        q, k, v = synth.queue_inputs(w.n, w.L, w.H, w.D, w.seed, device=dev, dtype=dt,
+                                     k_rho=w.k_rho, v_rho=w.v_rho)
+        cache = synth.build_cache(k, v)
+        out = torch.empty_like(q)
+        if w.n_text:
+            qx = synth.cross_queries(w.n, w.L, w.H, w.D, w.seed, dev, dt)
+            kt, vt = synth.text_inputs(w.n_text, w.H, w.D, w.seed, dev, dt)
+            ox = torch.empty_like(qx)
+    else:
+        q = synth.normal((w.n, w.L, w.H, w.D), w.seed, synth.Q_ID, dev, dt)
+        k = synth.normal((w.n, w.lkv, w.H, w.D), w.seed, synth.K_ID, dev, dt)
+        v = synth.normal((w.n, w.lkv, w.H, w.D), w.seed, synth.V_ID, dev, dt)
+        cache = None
+        out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs for {name} ready in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def dominant():
+        if w.kind == "queue":
+            ca.queue_step(q, k, v, cache, out=out, scale=w.scale, stream=stream)
+        else:
+            ca.full(q, k, v, out=out, scale=w.scale, stream=stream)
+
+    def step():
+        dominant()
+        if w.kind == "queue" and w.n_text:
+            ca.full(qx, kt, vt, out=ox, scale=w.scale, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, events around every launch of the dominant kernel
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        dominant()
+        ev[i][1].record(stream)
+        if w.kind == "queue" and w.n_text:
+            ca.full(qx, kt, vt, out=ox, scale=w.scale, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_per_step = total_ms / args.steps
+
+    flops_step = w.total_flops()
+    flops_dom = w.self_flops()
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+    dom_avg_ms = float(launch_ms.mean())
+    achieved = flops_dom / (dom_avg_ms * 1e-3) / 1e12
+
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": round(BF16_PEAK_TFLOPS, 1),
+        "unit": "TFLOP/s",
+        "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+        "traffic": None,
+        "kernel": "chunk_attn_fwd<128,bf16>",
+        "launch_ms_avg": round(dom_avg_ms, 4),
+        "launch_ms_min": round(float(launch_ms.min()), 4),
+        "launch_ms_p90": round(float(np.percentile(launch_ms, 90)), 4),
+    }
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        entry = tr.get(name)
+        if entry and entry.get("kernel_hash") == kernel_hash():
+            roofline["traffic"] = entry["bytes_per_launch"]
+
+    if args.copy_calibration:
+        n_bytes = 1 << 30
+        a = torch.empty(n_bytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {n_bytes} bytes read + written", file=sys.stderr,
+              flush=True)
+        del a, b
+
+    record = {
+        "metric": "chunk-attention TFLOP/s (exact FLOPs) + queue-steps/sec; % of MI355X bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": name,
+            "kind": w.kind,
+            "n_chunks": w.n,
+            "chunk_len": w.L,
+            "heads": w.H,
+            "head_dim": w.D,
+            "lkv": w.lkv if w.kind == "full" else None,
+            "kv_cache": "separate buffer" if cache is not None else None,
+            "text_tokens": w.n_text or None,
+            "flops_per_step": flops_step,
+        },
+        "queue_steps_per_s": round(1e3 / ms_per_step, 3),
+        "pct_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        record["cpu_baseline"] = cpu_baseline(w, q, k, v, cache, args.cpu_seconds)
+
+    print(json.dumps(record), flush=True)
+
+
+def cpu_baseline(w, q, k, v, cache, seconds):
+    """Times the fp64 oracle on host cores on a bounded sample of the workload.
+
+    Sample: random query rows (all heads equally likely) of chunk 0 and of
+    chunks >= 1 in their workload proportions; the oracle computes each row over
+    its full key/value set.  Throughput uses the same exact FLOP count per row
+    (4 * |R_c| * D), and queue-steps/s is extrapolated from it.
+    """
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(1234)
+    if w.kind == "queue":
+        chunks = [0, 1] if w.n > 1 else [0]
+        lo = max(chunks[-1] - 1, 0)
+        sub = lambda t: t[lo:chunks[-1] + 1].cpu()
+        qs, ks, vs = sub(q), sub(k), sub(v)
+        cs = None if cache is None else sub(cache)
+
+        def rows_for(count):
+            # chunk 0 carries 1 share of the work per L rows, chunks >= 1 carry 2 each
+            p1 = (2 * (w.n - 1)) / (2 * (w.n - 1) + 1) if w.n > 1 else 0.0
+            c = (rng.random(count) < p1).astype(np.int64)
+            return np.stack([c, rng.integers(0, w.H, count), rng.integers(0, w.L, count)], 1)
+
+        def flops(rows):
+            return float(sum(4 * (2 * w.L if c >= 1 else w.L) * w.D for c in rows[:, 0]))
+
+        run = lambda rows: oracle.queue_rows(qs, ks, vs, cs, rows, w.scale)
+    else:
+        qs, ks, vs = q.cpu(), k.cpu(), v.cpu()
+
+        def rows_for(count):
+            return np.stack([np.zeros(count, np.int64), rng.integers(0, w.H, count),
+                             rng.integers(0, w.L, count)], 1)
+
+        def flops(rows):
+            return float(len(rows) * 4 * w.lkv * w.D)
+
+        run = lambda rows: oracle.full_rows(qs, ks, vs, rows, w.scale)
+
+    probe = rows_for(64)
+    t0 = time.perf_counter()
+    run(probe)
+    dt = time.perf_counter() - t0
+    count = int(max(64, min(200000, 64 * seconds / max(dt, 1e-6))))
+    rows = rows_for(count)
+    t0 = time.perf_counter()
+    run(rows)
+    dt = time.perf_counter() - t0
+    tflops = flops(rows) / dt / 1e12
+    return {
+        "value": round(tflops, 6),
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{count} random query rows (all heads) of {w.name}, each over its full "
+                  f"key/value set; {dt:.1f} s; fp64",
+        "queue_steps_per_s_extrapolated": round(tflops * 1e12 / w.self_flops(), 8),
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,269 @@
+"""ctypes binding of the chunk-attention C ABI (include/chunkattn.h).
+
+Argument marshalling only: tensors become device pointers and sizes, the
+current torch stream becomes the HIP stream, status codes become exceptions.
+Every step of the computation runs in the HIP library; there is no fallback.
+If the library is missing the first call raises ChunkAttnUnavailable.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "lib", "libchunkattn.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "chunkattn.h")
+
+OK, EINVAL, EUNSUPPORTED, EDEVICE, ENOMEM, ELAUNCH = range(6)
+BF16, F32 = 0, 1
+PLAN_FIELDS = ("chunk", "head", "q_row0", "q_rows", "pred_chunk", "pred_rows", "own_rows")
+
+
+class ChunkAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"chunkattn status {status}: {message}")
+        self.status = status
+
+
+class ChunkAttnUnavailable(ImportError):
+    pass
+
+
+_lib = None
+
+
+def load_library():
+    """Loads lib/libchunkattn.so (raises ChunkAttnUnavailable if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ChunkAttnUnavailable(
+            f"{LIB_PATH} is missing; build it with `python -m chunked_spatio_temporal_amd._build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float
+    lib.chunkattn_block_rows.restype = i32
+    lib.chunkattn_create.restype = i32
+    lib.chunkattn_create.argtypes = [ctypes.POINTER(vp), i32, ctypes.c_uint]
+    lib.chunkattn_destroy.restype = i32
+    lib.chunkattn_destroy.argtypes = [vp]
+    lib.chunkattn_queue_step.restype = i32
+    lib.chunkattn_queue_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
+    lib.chunkattn_full.restype = i32
+    lib.chunkattn_full.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, f32, i32, vp]
+    lib.chunkattn_validate_queue_step.restype = i32
+    lib.chunkattn_validate_queue_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32]
+    lib.chunkattn_validate_full.restype = i32
+    lib.chunkattn_validate_full.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, f32, i32]
+    lib.chunkattn_status_string.restype = ctypes.c_char_p
+    lib.chunkattn_status_string.argtypes = [i32]
+    lib.chunkattn_last_error.restype = ctypes.c_char_p
+    lib.chunkattn_last_error.argtypes = [vp]
+    lib.chunkattn_plan_debug.restype = i32
+    lib.chunkattn_plan_debug.argtypes = [i32, i32, i32, i32, vp, i64, ctypes.POINTER(i64)]
+    lib.chunkattn_plan_device.restype = i32
+    lib.chunkattn_plan_device.argtypes = [vp, i32, i32, i32, vp, i64, vp]
+    lib.chunkattn_ctx_xcd_count.restype = i32
+    lib.chunkattn_ctx_xcd_count.argtypes = [vp]
+    _lib = lib
+    return lib
+
+
+def declared_symbols() -> list[str]:
+    """Names of the functions include/chunkattn.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(chunkattn_[a-z_]+)\s*\(", text)))
+
+
+def _check(rc: int, ctx_handle=None):
+    if rc != OK:
+        lib = load_library()
+        msg = lib.chunkattn_last_error(ctx_handle).decode()
+        raise ChunkAttnError(rc, msg or lib.chunkattn_status_string(rc).decode())
+
+
+def block_rows() -> int:
+    return int(load_library().chunkattn_block_rows())
+
+
+class Context:
+    """Owns a chunkattn_ctx bound to one device."""
+
+    def __init__(self, device: int = 0):
+        lib = load_library()
+        h = ctypes.c_void_p()
+        _check(lib.chunkattn_create(ctypes.byref(h), int(device), 0))
+        self.handle = h
+        self.device = int(device)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            load_library().chunkattn_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def xcd_count(self) -> int:
+        return int(load_library().chunkattn_ctx_xcd_count(self.handle))
+
+
+_contexts: dict[int, Context] = {}
+
+
+def create(device: int = 0) -> Context:
+    """The process-wide context of `device` (created on first use)."""
+    ctx = _contexts.get(device)
+    if ctx is None:
+        ctx = _contexts[device] = Context(device)
+    return ctx
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"chunkattn: unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require(t, name, dev):
+    if not t.is_cuda:
+        raise ValueError(f"chunkattn: {name} must be a GPU tensor")
+    if t.device != dev:
+        raise ValueError(f"chunkattn: {name} is on {t.device}, q on {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"chunkattn: {name} must be contiguous")
+
+
+def queue_step(q, k, v, kv_cache=None, out=None, scale=None, stream=None):
+    """One queue step: chunk c attends over [predecessor K/V ; own K/V].
+
+    q, k, v: [n_chunks, chunk_len, heads, head_dim] bf16/fp32 GPU tensors.
+    kv_cache: optional [n_chunks, 2, chunk_len, heads, head_dim] (slot c = K/V
+    of chunk c-1); None reads chunk c-1 from k/v in place.  Returns `out`.
+    """
+    import torch
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("chunkattn.queue_step: q, k, v must all be [n, L, H, D]")
+    n, L, H, D = q.shape
+    for name, t in (("k", k), ("v", v)):
+        _require(t, name, q.device)
+        if t.dtype != q.dtype:
+            raise TypeError(f"chunkattn.queue_step: {name} dtype {t.dtype} != q dtype {q.dtype}")
+    _require(q, "q", q.device)
+    if kv_cache is not None:
+        _require(kv_cache, "kv_cache", q.device)
+        if kv_cache.shape != (n, 2, L, H, D) or kv_cache.dtype != q.dtype:
+            raise ValueError("chunkattn.queue_step: kv_cache must be [n, 2, L, H, D] of q's dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", q.device)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("chunkattn.queue_step: out must match q")
+    scale = D ** -0.5 if scale is None else float(scale)
+    ctx = create(q.device.index or 0)
+    rc = load_library().chunkattn_queue_step(
+        ctx.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_cache), _ptr(out), L, n, H, D, scale,
+        _dtype_code(q), _stream(q, stream))
+    _check(rc, ctx.handle)
+    return out
+
+
+def full(q, k, v, out=None, scale=None, stream=None):
+    """Non-chunked attention of every query row over all K/V rows of its batch item.
+
+    q: [batch, lq, H, D]; k, v: [batch, lkv, H, D], or [1, lkv, H, D] shared by
+    the whole batch (kv stride 0, e.g. text tokens of one prompt).
+    """
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("chunkattn.full: q is [B, Lq, H, D]; k, v are [B or 1, Lkv, H, D]")
+    B, lq, H, D = q.shape
+    kb, lkv, Hk, Dk = k.shape
+    if (Hk, Dk) != (H, D) or kb not in (1, B):
+        raise ValueError("chunkattn.full: k/v heads/head_dim must match q; batch 1 or B")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, q.device)
+        if t.dtype != q.dtype:
+            raise TypeError(f"chunkattn.full: {name} dtype {t.dtype} != q dtype {q.dtype}")
+    stride = 0 if (kb == 1 and B > 1) else lkv * H * D
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", q.device)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("chunkattn.full: out must match q")
+    scale = D ** -0.5 if scale is None else float(scale)
+    ctx = create(q.device.index or 0)
+    rc = load_library().chunkattn_full(
+        ctx.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, lq, lkv, stride, H, D, scale,
+        _dtype_code(q), _stream(q, stream))
+    _check(rc, ctx.handle)
+    return out
+
+
+def plan_debug(chunk_len: int, n_chunks: int, heads: int, n_xcd: int = 8) -> np.ndarray:
+    """The queue-step launch plan computed on the host, [n_items, 7] int32."""
+    lib = load_library()
+    n = ctypes.c_longlong()
+    _check(lib.chunkattn_plan_debug(chunk_len, n_chunks, heads, n_xcd, None, 0, ctypes.byref(n)))
+    items = np.zeros((n.value, 7), np.int32)
+    _check(lib.chunkattn_plan_debug(chunk_len, n_chunks, heads, n_xcd,
+                                    items.ctypes.data_as(ctypes.c_void_p), n.value,
+                                    ctypes.byref(n)))
+    return items
+
+
+def plan_device(chunk_len: int, n_chunks: int, heads: int, device: int = 0):
+    """The same plan as decoded by the device kernel, [n_items, 7] int32 (GPU)."""
+    import torch
+    lib = load_library()
+    ctx = create(device)
+    n = ctypes.c_longlong()
+    _check(lib.chunkattn_plan_debug(chunk_len, n_chunks, heads, ctx.xcd_count, None, 0,
+                                    ctypes.byref(n)))
+    dev = torch.device("cuda", device)
+    items = torch.full((max(n.value, 1), 7), -7, dtype=torch.int32, device=dev)
+    _check(lib.chunkattn_plan_device(ctx.handle, chunk_len, n_chunks, heads,
+                                     ctypes.c_void_p(items.data_ptr()), n.value,
+                                     _stream(items, None)), ctx.handle)
+    return items[: n.value]
+
+
+def validate_queue_step(q_ptr, k_ptr, v_ptr, cache_ptr, out_ptr, chunk_len, n_chunks, heads,
+                        head_dim, scale, dtype):
+    """(status, message) of the device-free argument checks of queue_step."""
+    lib = load_library()
+    rc = lib.chunkattn_validate_queue_step(q_ptr, k_ptr, v_ptr, cache_ptr, out_ptr, chunk_len,
+                                           n_chunks, heads, head_dim, scale, dtype)
+    return rc, lib.chunkattn_last_error(None).decode()
+
+
+def validate_full(q_ptr, k_ptr, v_ptr, out_ptr, batch, lq, lkv, kv_batch_stride, heads,
+                  head_dim, scale, dtype):
+    """(status, message) of the device-free argument checks of full."""
+    lib = load_library()
+    rc = lib.chunkattn_validate_full(q_ptr, k_ptr, v_ptr, out_ptr, batch, lq, lkv,
+                                     kv_batch_stride, heads, head_dim, scale, dtype)
+    return rc, lib.chunkattn_last_error(None).decode()

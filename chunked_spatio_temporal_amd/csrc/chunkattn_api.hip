@@ -1,0 +1,368 @@
+// C-ABI entry points of the chunk-attention library (declared in
+// include/chunkattn.h): argument validation, the integer launch plan and the
+// kernel launch.  No allocation happens on the hot calls.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "attn_kernel.h"
+#include "chunkattn.h"
+
+struct chunkattn_ctx {
+  int device = 0;
+  int n_cu = 0;
+  int n_xcd = 1;
+  std::string arch;
+  std::string err;
+};
+
+namespace {
+
+using chunkattn::KernelArgs;
+using chunkattn::Plan;
+
+thread_local std::string g_thread_err;
+
+int set_err(std::string* sink, int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (sink) *sink = buf;
+  return code;
+}
+
+size_t elem_size(int dtype) { return dtype == CHUNKATTN_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+int check_common(std::string* err, int heads, int head_dim, float scale, int dtype) {
+  if (dtype != CHUNKATTN_BF16 && dtype != CHUNKATTN_F32)
+    return set_err(err, CHUNKATTN_EUNSUPPORTED, "dtype %d is not CHUNKATTN_BF16 or CHUNKATTN_F32",
+                   dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return set_err(err, CHUNKATTN_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (heads < 1) return set_err(err, CHUNKATTN_EINVAL, "heads must be >= 1 (got %d)", heads);
+  if (!std::isfinite(scale) || scale < 0.f)
+    return set_err(err, CHUNKATTN_EINVAL, "scale must be finite and >= 0 (got %g)",
+                   (double)scale);
+  return CHUNKATTN_OK;
+}
+
+// Largest element count accepted for one tensor: keeps every byte offset well
+// inside int64 and every row index of the kernel inside int32.
+constexpr long double kMaxElems = 4.0e18L;
+
+int validate_queue(std::string* err, const void* q, const void* k, const void* v,
+                   const void* kv_cache, const void* out, int L, int n, int heads, int head_dim,
+                   float scale, int dtype) {
+  int rc = check_common(err, heads, head_dim, scale, dtype);
+  if (rc) return rc;
+  if (L < 0 || n < 0)
+    return set_err(err, CHUNKATTN_EINVAL, "chunk_len (%d) and n_chunks (%d) must be >= 0", L, n);
+  if (L == 0 || n == 0) return CHUNKATTN_OK;
+  if (L > (1 << 30))
+    return set_err(err, CHUNKATTN_EUNSUPPORTED, "chunk_len %d too large (max 2^30)", L);
+  const long double elems = (long double)n * L * heads * head_dim;
+  if (elems * 2 > kMaxElems)
+    return set_err(err, CHUNKATTN_EINVAL, "tensor size overflows 64-bit offsets");
+  if ((long double)heads * head_dim > 2147483647.0L)
+    return set_err(err, CHUNKATTN_EINVAL, "heads * head_dim overflows int32");
+  if (!q || !k || !v || !out)
+    return set_err(err, CHUNKATTN_EINVAL, "q, k, v and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (kv_cache && !aligned16(kv_cache)))
+    return set_err(err, CHUNKATTN_EINVAL, "tensor pointers must be 16-byte aligned");
+  const size_t bytes = (size_t)elems * elem_size(dtype);
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
+      overlaps(out, bytes, v, bytes) || (kv_cache && overlaps(out, bytes, kv_cache, 2 * bytes)))
+    return set_err(err, CHUNKATTN_EINVAL, "out overlaps an input tensor");
+  const long double items =
+      (long double)n * heads * ((L + chunkattn::kBM - 1) / chunkattn::kBM);
+  if (items > 2147483647.0L)
+    return set_err(err, CHUNKATTN_EUNSUPPORTED, "too many work items for one launch");
+  return CHUNKATTN_OK;
+}
+
+int validate_full(std::string* err, const void* q, const void* k, const void* v,
+                  const void* out, int batch, int lq, int lkv, long long kv_stride, int heads,
+                  int head_dim, float scale, int dtype) {
+  int rc = check_common(err, heads, head_dim, scale, dtype);
+  if (rc) return rc;
+  if (batch < 0 || lq < 0)
+    return set_err(err, CHUNKATTN_EINVAL, "batch (%d) and lq (%d) must be >= 0", batch, lq);
+  if (kv_stride < 0)
+    return set_err(err, CHUNKATTN_EINVAL, "kv_batch_stride must be >= 0 (got %lld)", kv_stride);
+  if (batch == 0 || lq == 0) return CHUNKATTN_OK;
+  if (lkv < 1)
+    return set_err(err, CHUNKATTN_EINVAL, "lkv must be >= 1: attention over no keys (got %d)",
+                   lkv);
+  if (lq > (1 << 30) || lkv > (1 << 30))
+    return set_err(err, CHUNKATTN_EUNSUPPORTED, "lq/lkv too large (max 2^30)");
+  const long double row = (long double)heads * head_dim;
+  const long double qel = (long double)batch * lq * row;
+  const long double kvel = (long double)(batch - 1) * kv_stride + (long double)lkv * row;
+  if (qel > kMaxElems || kvel > kMaxElems)
+    return set_err(err, CHUNKATTN_EINVAL, "tensor size overflows 64-bit offsets");
+  if (row > 2147483647.0L)
+    return set_err(err, CHUNKATTN_EINVAL, "heads * head_dim overflows int32");
+  if (!q || !k || !v || !out)
+    return set_err(err, CHUNKATTN_EINVAL, "q, k, v and out must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      ((kv_stride * (long long)elem_size(dtype)) & 15))
+    return set_err(err, CHUNKATTN_EINVAL,
+                   "tensor pointers and the K/V batch stride must be 16-byte aligned");
+  const size_t es = elem_size(dtype);
+  const size_t qb = (size_t)qel * es, kb = (size_t)kvel * es;
+  if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kb) || overlaps(out, qb, v, kb))
+    return set_err(err, CHUNKATTN_EINVAL, "out overlaps an input tensor");
+  const long double items =
+      (long double)batch * heads * ((lq + chunkattn::kBM - 1) / chunkattn::kBM);
+  if (items > 2147483647.0L)
+    return set_err(err, CHUNKATTN_EUNSUPPORTED, "too many work items for one launch");
+  return CHUNKATTN_OK;
+}
+
+template <int D, typename T>
+hipError_t launch_t(const KernelArgs& a, hipStream_t stream) {
+  using TL = chunkattn::Tile<D>;
+  const dim3 grid((unsigned)a.plan.n_items);
+  hipLaunchKernelGGL((chunkattn::chunk_attn_fwd<D, T>), grid, dim3(chunkattn::kThreads),
+                     2 * TL::kBufBytes, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch(const KernelArgs& a, int head_dim, int dtype, hipStream_t stream) {
+  if (head_dim == 128)
+    return dtype == CHUNKATTN_BF16 ? launch_t<128, __bf16>(a, stream)
+                                   : launch_t<128, float>(a, stream);
+  return dtype == CHUNKATTN_BF16 ? launch_t<64, __bf16>(a, stream)
+                                 : launch_t<64, float>(a, stream);
+}
+
+// Makes the context's device current for the duration of a call.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+int run(chunkattn_ctx* ctx, const KernelArgs& a, int head_dim, int dtype, void* stream) {
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return set_err(&ctx->err, CHUNKATTN_EDEVICE, "cannot make device %d current",
+                            ctx->device);
+  const hipError_t e = launch(a, head_dim, dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return set_err(&ctx->err, CHUNKATTN_ELAUNCH, "kernel launch failed: %s",
+                   hipGetErrorString(e));
+  ctx->err.clear();
+  return CHUNKATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int chunkattn_block_rows(void) { return chunkattn::kBM; }
+
+int chunkattn_create(chunkattn_ctx** out, int device_ordinal, unsigned flags) {
+  if (!out) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "out must be non-NULL");
+  *out = nullptr;
+  if (flags != 0) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "flags must be 0");
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || device_ordinal < 0 || device_ordinal >= count)
+    return set_err(&g_thread_err, CHUNKATTN_EDEVICE, "no HIP device %d (found %d)",
+                   device_ordinal, count);
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device_ordinal) != hipSuccess)
+    return set_err(&g_thread_err, CHUNKATTN_EDEVICE, "cannot query device %d", device_ordinal);
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return set_err(&g_thread_err, CHUNKATTN_EUNSUPPORTED,
+                   "device %d is %s; this library is built for gfx950 only", device_ordinal,
+                   prop.gcnArchName);
+  chunkattn_ctx* ctx = new (std::nothrow) chunkattn_ctx();
+  if (!ctx) return set_err(&g_thread_err, CHUNKATTN_ENOMEM, "context allocation failed");
+  ctx->device = device_ordinal;
+  ctx->n_cu = prop.multiProcessorCount;
+  ctx->arch = prop.gcnArchName;
+  int xcc = 0;
+  if (hipDeviceGetAttribute(&xcc, hipDeviceAttributeNumberOfXccs, device_ordinal) ==
+          hipSuccess &&
+      xcc > 0)
+    ctx->n_xcd = xcc;
+  *out = ctx;
+  return CHUNKATTN_OK;
+}
+
+int chunkattn_destroy(chunkattn_ctx* ctx) {
+  delete ctx;
+  return CHUNKATTN_OK;
+}
+
+int chunkattn_ctx_xcd_count(const chunkattn_ctx* ctx) { return ctx ? ctx->n_xcd : 0; }
+
+int chunkattn_validate_queue_step(const void* q, const void* k, const void* v,
+                                  const void* kv_cache, const void* out, int chunk_len,
+                                  int n_chunks, int heads, int head_dim, float scale,
+                                  int dtype) {
+  g_thread_err.clear();
+  return validate_queue(&g_thread_err, q, k, v, kv_cache, out, chunk_len, n_chunks, heads,
+                        head_dim, scale, dtype);
+}
+
+int chunkattn_validate_full(const void* q, const void* k, const void* v, const void* out,
+                            int batch, int lq, int lkv, long long kv_batch_stride, int heads,
+                            int head_dim, float scale, int dtype) {
+  g_thread_err.clear();
+  return validate_full(&g_thread_err, q, k, v, out, batch, lq, lkv, kv_batch_stride, heads,
+                       head_dim, scale, dtype);
+}
+
+int chunkattn_queue_step(chunkattn_ctx* ctx, const void* q, const void* k, const void* v,
+                         const void* kv_cache, void* out, int chunk_len, int n_chunks,
+                         int heads, int head_dim, float scale, int dtype, void* hip_stream) {
+  if (!ctx) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "ctx must be non-NULL");
+  int rc = validate_queue(&ctx->err, q, k, v, kv_cache, out, chunk_len, n_chunks, heads,
+                          head_dim, scale, dtype);
+  if (rc) return rc;
+  if (chunk_len == 0 || n_chunks == 0) {
+    ctx->err.clear();
+    return CHUNKATTN_OK;
+  }
+  const int64_t per_chunk = (int64_t)chunk_len * heads * head_dim;
+  const size_t es = elem_size(dtype);
+  KernelArgs a;
+  a.plan = chunkattn::make_plan(n_chunks, 1, heads, chunk_len, chunk_len, chunk_len,
+                                chunkattn::kBM, ctx->n_xcd);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.q_bstride = per_chunk;
+  a.kv_bstride = per_chunk;
+  if (kv_cache) {
+    a.pk = kv_cache;
+    a.pv = static_cast<const unsigned char*>(kv_cache) + (size_t)per_chunk * es;
+    a.p_bstride = 2 * per_chunk;
+    a.pred_shift = 0;
+  } else {
+    a.pk = k;
+    a.pv = v;
+    a.p_bstride = per_chunk;
+    a.pred_shift = 1;
+  }
+  a.row_stride = heads * head_dim;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return run(ctx, a, head_dim, dtype, hip_stream);
+}
+
+int chunkattn_full(chunkattn_ctx* ctx, const void* q, const void* k, const void* v, void* out,
+                   int batch, int lq, int lkv, long long kv_batch_stride, int heads,
+                   int head_dim, float scale, int dtype, void* hip_stream) {
+  if (!ctx) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "ctx must be non-NULL");
+  int rc = validate_full(&ctx->err, q, k, v, out, batch, lq, lkv, kv_batch_stride, heads,
+                         head_dim, scale, dtype);
+  if (rc) return rc;
+  if (batch == 0 || lq == 0) {
+    ctx->err.clear();
+    return CHUNKATTN_OK;
+  }
+  KernelArgs a;
+  a.plan = chunkattn::make_plan(batch, batch, heads, lq, lkv, 0, chunkattn::kBM, ctx->n_xcd);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.pk = nullptr;
+  a.pv = nullptr;
+  a.o = out;
+  a.q_bstride = (int64_t)lq * heads * head_dim;
+  a.kv_bstride = kv_batch_stride;
+  a.p_bstride = 0;
+  a.pred_shift = 0;
+  a.row_stride = heads * head_dim;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return run(ctx, a, head_dim, dtype, hip_stream);
+}
+
+const char* chunkattn_status_string(int status) {
+  switch (status) {
+    case CHUNKATTN_OK: return "ok";
+    case CHUNKATTN_EINVAL: return "invalid argument";
+    case CHUNKATTN_EUNSUPPORTED: return "unsupported";
+    case CHUNKATTN_EDEVICE: return "device error";
+    case CHUNKATTN_ENOMEM: return "out of host memory";
+    case CHUNKATTN_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* chunkattn_last_error(const chunkattn_ctx* ctx) {
+  return ctx ? ctx->err.c_str() : g_thread_err.c_str();
+}
+
+int chunkattn_plan_debug(int chunk_len, int n_chunks, int heads, int n_xcd, int* items,
+                         long long cap, long long* n_items) {
+  g_thread_err.clear();
+  if (!n_items) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "n_items must be non-NULL");
+  if (chunk_len < 0 || n_chunks < 0 || heads < 1 || cap < 0 || (cap > 0 && !items))
+    return set_err(&g_thread_err, CHUNKATTN_EINVAL, "bad plan_debug arguments");
+  *n_items = 0;
+  if (chunk_len == 0 || n_chunks == 0) return CHUNKATTN_OK;
+  const Plan p = chunkattn::make_plan(n_chunks, 1, heads, chunk_len, chunk_len, chunk_len,
+                                      chunkattn::kBM, n_xcd);
+  *n_items = p.n_items;
+  for (int64_t slot = 0; slot < p.n_items && slot < cap; ++slot) {
+    const chunkattn::Item it =
+        chunkattn::decode(p, chunkattn::slot_to_work(slot, p.n_items, p.n_xcd));
+    int* r = items + slot * 7;
+    r[0] = it.b;
+    r[1] = it.h;
+    r[2] = it.q0;
+    r[3] = it.q_rows;
+    r[4] = it.pred_rows > 0 ? it.b - 1 : -1;
+    r[5] = it.pred_rows;
+    r[6] = it.own_rows;
+  }
+  return CHUNKATTN_OK;
+}
+
+int chunkattn_plan_device(chunkattn_ctx* ctx, int chunk_len, int n_chunks, int heads,
+                          int* dev_items, long long cap, void* hip_stream) {
+  if (!ctx) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "ctx must be non-NULL");
+  if (chunk_len < 0 || n_chunks < 0 || heads < 1 || cap < 0 || (cap > 0 && !dev_items))
+    return set_err(&ctx->err, CHUNKATTN_EINVAL, "bad plan_device arguments");
+  if (chunk_len == 0 || n_chunks == 0 || cap == 0) return CHUNKATTN_OK;
+  const Plan p = chunkattn::make_plan(n_chunks, 1, heads, chunk_len, chunk_len, chunk_len,
+                                      chunkattn::kBM, ctx->n_xcd);
+  const int64_t n = p.n_items < cap ? p.n_items : cap;
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return set_err(&ctx->err, CHUNKATTN_EDEVICE, "cannot make device current");
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(chunkattn::plan_dump, dim3(blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(hip_stream), p, dev_items, (int64_t)cap);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return set_err(&ctx->err, CHUNKATTN_ELAUNCH, "plan_dump launch failed: %s",
+                   hipGetErrorString(e));
+  ctx->err.clear();
+  return CHUNKATTN_OK;
+}
+
+}  // extern "C"

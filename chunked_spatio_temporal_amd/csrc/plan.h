@@ -1,0 +1,102 @@
+// Integer work plan of the chunk-attention launch: which (chunk, head, query
+// tile) each workgroup computes, and which key/value rows it walks.
+//
+// One work item = one (batch item b, head h, query tile t) with query rows
+// [t*BM, min(Lq, (t+1)*BM)).  Its logical key/value rows are [0, pred + own):
+// logical row j < pred reads the predecessor segment (the cached K/V of the
+// chunk processed just before, DualParal write-up section 三), j >= pred reads
+// row j - pred of the item's own K/V.  Nothing is concatenated in memory.
+//
+// Order.  Items of batch entries that have a predecessor (chunks 1..n-1 of a
+// queue step) come first, because they walk twice the key rows; chunk 0, which
+// has none, fills the tail of the launch.  Within a group the order is
+// (b, h, t) with t fastest, so consecutive items share one chunk/head's K/V.
+//
+// Die-aware launch order.  Workgroup ids are handed to the accelerator dies
+// round-robin (id % n_xcd).  slot_to_work() renumbers so that die x processes
+// one contiguous range of work items; the query tiles of one (chunk, head) then
+// run together on one die and share that die's L2 copy of the K/V tiles.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define CA_HD __host__ __device__ __forceinline__
+#else
+#define CA_HD inline
+#endif
+
+namespace chunkattn {
+
+struct Plan {
+  int n_batch;     // chunks (queue step) or batch items (full attention)
+  int first_pred;  // batch entries b >= first_pred have a predecessor segment
+  int heads;
+  int lq;          // query rows per batch entry
+  int lown;        // own key/value rows per batch entry
+  int lpred;       // predecessor rows (entries b >= first_pred)
+  int bm;          // query rows per work item
+  int n_qtiles;    // ceil(lq / bm)
+  int n_xcd;       // dies for the launch-order renumbering (>= 1)
+  int64_t n_items;
+  int64_t n_items_pred;  // items of entries with a predecessor (scheduled first)
+};
+
+struct Item {
+  int b, h, q0, q_rows, pred_rows, own_rows;
+};
+
+CA_HD Plan make_plan(int n_batch, int first_pred, int heads, int lq, int lown, int lpred,
+                     int bm, int n_xcd) {
+  Plan p;
+  p.n_batch = n_batch;
+  p.first_pred = first_pred < n_batch ? first_pred : n_batch;
+  p.heads = heads;
+  p.lq = lq;
+  p.lown = lown;
+  p.lpred = lpred;
+  p.bm = bm;
+  p.n_qtiles = (lq + bm - 1) / bm;
+  p.n_xcd = n_xcd < 1 ? 1 : n_xcd;
+  const int64_t per_entry = (int64_t)heads * p.n_qtiles;
+  p.n_items = (int64_t)n_batch * per_entry;
+  p.n_items_pred = (int64_t)(n_batch - p.first_pred) * per_entry;
+  return p;
+}
+
+// Launch slot (workgroup id) -> work index.  A bijection on [0, n): die x
+// (= slot % n_xcd) gets the contiguous range of work indices that starts at
+// x*per + min(x, extra), where per = n / n_xcd and the first `extra` dies
+// take one more.
+CA_HD int64_t slot_to_work(int64_t slot, int64_t n, int n_xcd) {
+  if (n_xcd <= 1) return slot;
+  const int64_t per = n / n_xcd, extra = n % n_xcd;
+  const int64_t x = slot % n_xcd, local = slot / n_xcd;
+  // slots of the last round exist only for dies x < extra
+  return x * per + (x < extra ? x : extra) + local;
+}
+
+CA_HD Item decode(const Plan& p, int64_t w) {
+  const int64_t per_entry = (int64_t)p.heads * p.n_qtiles;
+  int64_t b, rem;
+  if (w < p.n_items_pred) {
+    b = p.first_pred + w / per_entry;
+    rem = w % per_entry;
+  } else {
+    const int64_t w2 = w - p.n_items_pred;
+    b = w2 / per_entry;
+    rem = w2 % per_entry;
+  }
+  Item it;
+  it.b = (int)b;
+  it.h = (int)(rem / p.n_qtiles);
+  const int t = (int)(rem % p.n_qtiles);
+  it.q0 = t * p.bm;
+  const int left = p.lq - it.q0;
+  it.q_rows = left < p.bm ? left : p.bm;
+  it.pred_rows = b >= p.first_pred ? p.lpred : 0;
+  it.own_rows = p.lown;
+  return it;
+}
+
+}  // namespace chunkattn

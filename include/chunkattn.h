@@ -1,0 +1,174 @@
+/*
+ * chunkattn -- chunked spatio-temporal attention for a DualParal-style FIFO
+ * chunk queue on AMD Instinct MI355X (gfx950).  C ABI: plain pointers and
+ * sizes, no C++ types, no exceptions across the boundary.
+ *
+ * The operation (cited by page and section):
+ *
+ *   DualParal write-up, techwalker.com, "双重并行：让AI视频生成突破时长限制",
+ *   section 二 (FIFO queue and block-wise denoising): the video is cut into
+ *   fixed-size, non-overlapping temporal chunks held in a FIFO queue, every
+ *   chunk at its own noise level, all of them processed in one step and fed
+ *   from the tail to the head.  Section 三 (feature cache): the self-attention
+ *   K/V of the chunk processed just before are kept and reused by the next
+ *   chunk, so no concatenated copy of the neighbouring chunk is built; only
+ *   self-attention uses the cache, cross-attention stays per chunk.
+ *   Video-diffusion survey, intelliparadigm.com, "视频扩散模型：核心技术挑战与
+ *   前沿进展", section 2.1 item 2: spatio-temporal attention attends jointly
+ *   over all tokens of the frames in its window.
+ *
+ * Reading.  Chunk c (0-based, processing order) attends over
+ *   R_c = [predecessor K/V: chunk c-1's rows 0..L-1, only if c >= 1] ++ [own rows 0..L-1]
+ * with plain softmax attention, no mask inside R_c:
+ *   O[c,r,h,:] = softmax_j(scale * <Q[c,r,h,:], K_j[h,:]>) . V_j[h,:]
+ * Chunk 0 has a zero-length cache.
+ *
+ * Layouts (row-major, element = one bf16 or fp32 value):
+ *   q, k, v, out : [n_chunks][chunk_len][heads][head_dim]   (token-major, as a
+ *                  DiT's activations; a chunk's tokens are frame-major f,y,x,
+ *                  which attention does not depend on)
+ *   kv_cache     : [n_chunks][2][chunk_len][heads][head_dim]; slot c holds the
+ *                  predecessor's K (index 0) then V (index 1); slot 0 is never read.
+ *
+ * Numerics.  Q.K^T and P.V run on bf16 matrix cores with fp32 accumulation and
+ * an fp32 online softmax; P is rounded to bf16 before the P.V product and the
+ * softmax denominator is summed from the same rounded P.  dtype F32 means fp32
+ * storage in and out, rounded to bf16 (nearest-even) on load.  bf16 outputs are
+ * rounded nearest-even.  Results are bitwise deterministic run to run, and the
+ * separate-cache and in-place-predecessor forms give bitwise-equal outputs.
+ *
+ * Ownership and asynchrony.  Every tensor pointer is device memory owned by the
+ * caller and must stay valid until the stream work completes.  The library
+ * owns only the context.  queue_step and full make no allocation: they
+ * validate, enqueue one kernel on hip_stream (NULL = the legacy default
+ * stream) and return; a device fault surfaces at the caller's next
+ * synchronisation.  One context may be used by one host thread at a time;
+ * separate contexts are independent.
+ *
+ * Errors.  Every call returns a chunkattn_status synchronously, before any
+ * launch, for bad arguments; chunkattn_last_error() then holds a one-line
+ * explanation.  Nothing in the library calls exit() or abort().
+ */
+#ifndef CHUNKATTN_H
+#define CHUNKATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct chunkattn_ctx chunkattn_ctx; /* opaque, library-owned */
+
+typedef enum {
+    CHUNKATTN_OK = 0,
+    CHUNKATTN_EINVAL = 1,       /* bad argument: null/misaligned pointer, size, aliasing */
+    CHUNKATTN_EUNSUPPORTED = 2, /* head_dim, dtype or device not supported */
+    CHUNKATTN_EDEVICE = 3,      /* HIP runtime error outside a launch */
+    CHUNKATTN_ENOMEM = 4,       /* host allocation of the context failed */
+    CHUNKATTN_ELAUNCH = 5       /* the kernel launch was rejected */
+} chunkattn_status;
+
+typedef enum {
+    CHUNKATTN_BF16 = 0, /* bf16 storage in and out */
+    CHUNKATTN_F32 = 1   /* fp32 storage in and out (operands rounded to bf16) */
+} chunkattn_dtype;
+
+/* Query rows handled by one work item (one workgroup). */
+int chunkattn_block_rows(void);
+
+/*
+ * Creates a context bound to HIP device `device_ordinal`.  Fails with
+ * CHUNKATTN_EUNSUPPORTED unless the device is gfx950, CHUNKATTN_EDEVICE if the
+ * ordinal is invalid.  `flags` must be 0.  On success *out owns the context;
+ * release it with chunkattn_destroy.
+ */
+int chunkattn_create(chunkattn_ctx **out, int device_ordinal, unsigned flags);
+
+/* Releases a context (NULL is accepted). */
+int chunkattn_destroy(chunkattn_ctx *ctx);
+
+/*
+ * One queue step: every chunk c in [0, n_chunks) attends over R_c (see above),
+ * for every head and query row, in one launch on hip_stream.
+ *
+ *   q, k, v   [n_chunks][chunk_len][heads][head_dim], device, 16-byte aligned.
+ *   kv_cache  [n_chunks][2][chunk_len][heads][head_dim] separate predecessor
+ *             cache, or NULL to read chunk c-1's K/V from k and v in place.
+ *   out       same shape and dtype as q; must not overlap any input.
+ *   chunk_len, n_chunks  >= 0 (either 0: nothing to do, returns OK).
+ *   heads >= 1; head_dim 64 or 128; scale finite and >= 0 (applied to Q.K^T
+ *   before the softmax; 1/sqrt(head_dim) is the usual value).
+ *   dtype     chunkattn_dtype of q, k, v, kv_cache and out.
+ *   hip_stream  hipStream_t, or NULL.
+ */
+int chunkattn_queue_step(chunkattn_ctx *ctx, const void *q, const void *k, const void *v,
+                         const void *kv_cache, void *out, int chunk_len, int n_chunks,
+                         int heads, int head_dim, float scale, int dtype, void *hip_stream);
+
+/*
+ * Non-chunked attention: every query row of batch item b attends over all lkv
+ * rows of its K/V (the full-sequence attention the chunked form avoids, and
+ * the per-chunk cross-attention to text tokens, which uses no cache).
+ *
+ *   q, out  [batch][lq][heads][head_dim]
+ *   k, v    batch item b at element offset b * kv_batch_stride, each
+ *           [lkv][heads][head_dim]; kv_batch_stride = 0 shares one K/V
+ *           (e.g. one prompt's text tokens) across the batch.
+ *   batch, lq >= 0 (either 0: returns OK); lkv >= 1; kv_batch_stride >= 0.
+ *   Other arguments as for chunkattn_queue_step.
+ */
+int chunkattn_full(chunkattn_ctx *ctx, const void *q, const void *k, const void *v, void *out,
+                   int batch, int lq, int lkv, long long kv_batch_stride, int heads,
+                   int head_dim, float scale, int dtype, void *hip_stream);
+
+/*
+ * Argument checks of chunkattn_queue_step / chunkattn_full without a device:
+ * the same validation those calls perform before launching.  Pointers are not
+ * dereferenced.  The explanation of a failure is in chunkattn_last_error(NULL).
+ */
+int chunkattn_validate_queue_step(const void *q, const void *k, const void *v,
+                                  const void *kv_cache, const void *out, int chunk_len,
+                                  int n_chunks, int heads, int head_dim, float scale,
+                                  int dtype);
+int chunkattn_validate_full(const void *q, const void *k, const void *v, const void *out,
+                            int batch, int lq, int lkv, long long kv_batch_stride, int heads,
+                            int head_dim, float scale, int dtype);
+
+/* Static description of a status code. */
+const char *chunkattn_status_string(int status);
+
+/*
+ * Explanation of the last failing call on this context, or of the last failing
+ * validate call on this thread when ctx is NULL.  Empty string if none.  The
+ * pointer stays valid until the next call on the same context/thread.
+ */
+const char *chunkattn_last_error(const chunkattn_ctx *ctx);
+
+/*
+ * The integer work plan of a queue step, without a device: one record of 7
+ * ints per workgroup, in launch order (workgroup id 0, 1, ...):
+ *   (chunk, head, q_row0, q_rows, pred_chunk, pred_rows, own_rows)
+ * pred_chunk is c-1 when the chunk reads a predecessor (pred_rows = chunk_len),
+ * else -1 (pred_rows = 0).  n_xcd is the number of accelerator dies the
+ * workgroups are spread over (8 on MI355X; 1 disables the die-aware order).
+ * Writes at most `cap` records to `items` (may be NULL when cap is 0) and the
+ * total count to *n_items.
+ */
+int chunkattn_plan_debug(int chunk_len, int n_chunks, int heads, int n_xcd, int *items,
+                         long long cap, long long *n_items);
+
+/*
+ * The same plan as decoded on the device by the attention kernel's own decode
+ * routine: writes n_items * 7 ints to device memory `dev_items` on hip_stream,
+ * using the context's die count.  For bit-exact tests of the device decode.
+ */
+int chunkattn_plan_device(chunkattn_ctx *ctx, int chunk_len, int n_chunks, int heads,
+                          int *dev_items, long long cap, void *hip_stream);
+
+/* Number of accelerator dies (XCDs) the context uses for its launch order. */
+int chunkattn_ctx_xcd_count(const chunkattn_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CHUNKATTN_H */

@@ -1,0 +1,317 @@
+"""GPU parity of the HIP queue step and full attention against the fp64 oracle.
+
+Every test calls the C-ABI library through its Python binding and compares
+with the oracle on the same seeded inputs (chunked_spatio_temporal_amd.synth).
+Small shapes are compared element by element over the whole output; the
+full-size workloads (the same launch configuration the benchmark times) are
+compared on sampled rows, which the oracle computes one by one on the
+sub-problem of chunks c-1 and c, plus properties that hold at any size.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunked_spatio_temporal_amd import chunkattn as ca
+from chunked_spatio_temporal_amd import configs, synth
+from parity_util import assert_parity, error_stats, to_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ca.load_library()  # raises if the HIP library is not built
+    yield
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_queue(q, k, v, cache=None, scale=None):
+    out = ca.queue_step(q, k, v, cache, scale=scale)
+    torch.cuda.synchronize()
+    return out
+
+
+# ------------------------------------------------------------------ small / exact
+
+def test_tiny_config_full_parity():
+    w = configs.WORKLOADS["tiny"]
+    say("case tiny", w)
+    q, k, v = synth.queue_inputs(w.n, w.L, w.H, w.D, w.seed, device=DEV, dtype=torch.float32)
+    cache = synth.build_cache(k, v)
+    ref = oracle.queue_step(q, k, v, None, scale=w.scale)
+    out_alias = run_queue(q, k, v, None, w.scale)
+    out_cache = run_queue(q, k, v, cache, w.scale)
+    assert out_alias.dtype == torch.float32
+    s = assert_parity(to_f64(out_alias), ref, "tiny alias")
+    say("tiny stats", s)
+    assert torch.equal(out_alias, out_cache), "alias and cache modes differ"
+
+
+SHAPES = [
+    # n, L, H, D, dtype
+    (1, 1, 1, 64, torch.bfloat16),
+    (5, 1, 2, 128, torch.bfloat16),
+    (2, 31, 1, 128, torch.bfloat16),
+    (3, 64, 2, 64, torch.bfloat16),
+    (4, 97, 3, 128, torch.bfloat16),
+    (2, 128, 1, 128, torch.float32),
+    (3, 200, 2, 128, torch.bfloat16),
+    (2, 333, 1, 64, torch.float32),
+    (5, 129, 2, 128, torch.bfloat16),
+    (1, 300, 3, 128, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s[:4])) + str(s[4])[-4:])
+def test_ragged_shapes_full_parity(shape):
+    n, L, H, D, dt = shape
+    say("case ragged", shape)
+    q, k, v = synth.queue_inputs(n, L, H, D, seed=100 + L, device=DEV, dtype=dt, k_rho=0.9)
+    cache = synth.build_cache(k, v)
+    ref = oracle.queue_step(q, k, v, None)
+    a = run_queue(q, k, v, None)
+    b = run_queue(q, k, v, cache)
+    assert_parity(to_f64(a), ref, f"ragged {shape}")
+    assert torch.equal(a, b), "alias and cache modes differ"
+
+
+def test_deterministic_and_order_independent_of_stream_state():
+    q, k, v = synth.queue_inputs(4, 200, 3, 128, seed=7, device=DEV)
+    a = run_queue(q, k, v)
+    b = run_queue(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_guard_bands_and_cache_slot0_never_read():
+    n, L, H, D = 3, 150, 2, 128
+    q, k, v = synth.queue_inputs(n, L, H, D, seed=8, device=DEV)
+    pad = 4096  # elements of NaN before and after every tensor
+    def padded(t):
+        buf = torch.full((t.numel() + 2 * pad,), float("nan"), dtype=t.dtype, device=DEV)
+        buf[pad:pad + t.numel()].copy_(t.reshape(-1))
+        return buf, buf[pad:pad + t.numel()].view(t.shape)
+    _, qp = padded(q)
+    _, kp = padded(k)
+    _, vp = padded(v)
+    cache = synth.build_cache(k, v)  # slot 0 is NaN
+    assert torch.isnan(cache[0]).all()
+    _, cp = padded(cache)
+    obuf, op = padded(torch.zeros_like(q))
+    ca.queue_step(qp, kp, vp, cp, out=op)
+    torch.cuda.synchronize()
+    assert torch.isfinite(op).all()
+    assert torch.isnan(obuf[:pad]).all() and torch.isnan(obuf[pad + q.numel():]).all(), \
+        "writes outside out"
+    ref = run_queue(q, k, v)
+    assert torch.equal(op, ref)
+
+
+def test_range_fingerprint_bit_exact():
+    """Q = 0 makes every weight exactly 1, so O[c,r,h,d] = (number of tokens t
+    in R_c with (t + 7h) mod D == d) / |R_c|, with t the token's global index.
+    The kernel's fp32 sums of ones are exact, so the bf16 output must equal the
+    rounded rational exactly: a key/value row shifted by one, a wrong chunk or
+    head, or a dropped segment changes some entries."""
+    n, L, H, D = 4, 300, 3, 128
+    q = torch.zeros((n, L, H, D), dtype=torch.bfloat16, device=DEV)
+    k = synth.normal((n, L, H, D), 9, 2, DEV)
+    t = torch.arange(n * L, device=DEV).view(n, L, 1, 1)
+    hh = torch.arange(H, device=DEV).view(1, 1, H, 1)
+    d = torch.arange(D, device=DEV).view(1, 1, 1, D)
+    v = (((t + 7 * hh) % D) == d).to(torch.bfloat16)
+    cache = synth.build_cache(k, v)
+    exp = np.zeros((n, L, H, D))
+    for c in range(n):
+        toks = np.arange(max(c - 1, 0) * L, (c + 1) * L)
+        for h in range(H):
+            counts = np.bincount((toks + 7 * h) % D, minlength=D)
+            exp[c, :, h, :] = counts / len(toks)
+    exp_bf16 = torch.from_numpy(exp).float().to(torch.bfloat16)
+    for cc in (None, cache):
+        out = run_queue(q, k, v, cc)
+        assert torch.equal(out.cpu(), exp_bf16), "fingerprint mismatch"
+
+
+def test_constant_v_returned_exactly():
+    n, L, H, D = 3, 257, 2, 128
+    q, k, _ = synth.queue_inputs(n, L, H, D, seed=10, device=DEV)
+    cvec = synth.normal((1, 1, H, D), 10, 9, DEV)
+    v = cvec.expand(n, L, H, D).contiguous()
+    out = run_queue(q, k, v)
+    assert torch.equal(out, v)
+
+
+def test_scale_zero_is_uniform_mean():
+    n, L, H, D = 3, 100, 2, 64
+    q, k, v = synth.queue_inputs(n, L, H, D, seed=11, device=DEV, dtype=torch.float32)
+    out = run_queue(q, k, v, None, scale=0.0)
+    ref = oracle.queue_step(q, k, v, None, scale=0.0)
+    assert_parity(to_f64(out), ref, "scale 0")
+
+
+def test_empty_inputs_are_noops():
+    q = torch.empty((0, 16, 2, 128), dtype=torch.bfloat16, device=DEV)
+    out = ca.queue_step(q, q, q)
+    assert out.shape == q.shape
+    q1 = torch.randn((2, 0, 2, 128), device=DEV).to(torch.bfloat16)
+    assert ca.queue_step(q1, q1, q1).shape == q1.shape
+    qf = torch.empty((0, 5, 2, 128), dtype=torch.bfloat16, device=DEV)
+    kf = torch.randn((1, 7, 2, 128), device=DEV).to(torch.bfloat16)
+    assert ca.full(qf, kf, kf).shape == qf.shape
+
+
+def test_errors_are_raised_not_launched():
+    q, k, v = synth.queue_inputs(2, 16, 2, 96, seed=1, device=DEV)
+    with pytest.raises(ca.ChunkAttnError) as e:
+        ca.queue_step(q, k, v)
+    assert e.value.status == ca.EUNSUPPORTED
+    q, k, v = synth.queue_inputs(2, 16, 2, 128, seed=1, device=DEV)
+    with pytest.raises(ca.ChunkAttnError) as e:
+        ca.queue_step(q, k, v, scale=-1.0)
+    assert e.value.status == ca.EINVAL
+
+
+def test_device_plan_equals_host_plan():
+    ctx = ca.create(0)
+    say("xcd count", ctx.xcd_count)
+    for (L, n, H) in [(128, 4, 2), (6240, 8, 40), (97, 5, 3), (14400, 16, 40)]:
+        dev = ca.plan_device(L, n, H).cpu().numpy()
+        host = ca.plan_debug(L, n, H, ctx.xcd_count)
+        np.testing.assert_array_equal(dev, host)
+
+
+# -------------------------------------------------------------------- full attention
+
+@pytest.mark.parametrize("B,lq,lkv,H,D,shared", [(1, 300, 300, 2, 128, False),
+                                                 (3, 200, 77, 2, 128, True),
+                                                 (2, 129, 1, 1, 64, False),
+                                                 (4, 64, 512, 3, 128, True)])
+def test_full_small_parity(B, lq, lkv, H, D, shared):
+    say("case full", B, lq, lkv, H, D, shared)
+    q = synth.normal((B, lq, H, D), 12, 1, DEV)
+    kb = 1 if shared else B
+    k = synth.normal((kb, lkv, H, D), 12, 2, DEV)
+    v = synth.normal((kb, lkv, H, D), 12, 3, DEV)
+    out = ca.full(q, k, v)
+    torch.cuda.synchronize()
+    ref = oracle.full(q, k, v)
+    assert_parity(to_f64(out), ref, "full small")
+
+
+def test_single_chunk_queue_equals_full_bitwise():
+    q, k, v = synth.queue_inputs(1, 333, 2, 128, seed=13, device=DEV)
+    a = run_queue(q, k, v)
+    b = ca.full(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# -------------------------------------------------------------------- full-size workloads
+
+def sample_rows(n, L, H, rng, per=24):
+    bm = ca.block_rows()
+    chunks = sorted(c for c in {0, 1, n - 1, int(rng.integers(0, n))} if c < n)
+    heads = sorted({0, H - 1, int(rng.integers(0, H))})
+    fixed = {0, 1, bm - 1, bm, L - 1, L - 2, (L // bm) * bm, max(L - bm, 0)}
+    rows = []
+    for c in chunks:
+        for h in heads:
+            rs = set(r for r in fixed if 0 <= r < L)
+            rs |= set(rng.integers(0, L, per).tolist())
+            rows += [(c, h, r) for r in sorted(rs)]
+    return np.array(rows, np.int64)
+
+
+def queue_rows_oracle(q, k, v, cache, rows, scale):
+    """Oracle rows of the full problem, computed on the sub-problem [c-1, c]."""
+    out = np.empty((len(rows), q.shape[-1]))
+    for c in np.unique(rows[:, 0]):
+        lo = max(int(c) - 1, 0)
+        sub = lambda t: t[lo:c + 1].cpu()
+        sel = rows[:, 0] == c
+        r = rows[sel].copy()
+        r[:, 0] -= lo
+        out[sel] = oracle.queue_rows(sub(q), sub(k), sub(v),
+                                     None if cache is None else sub(cache), r, scale)
+    return out
+
+
+def gather_rows(out, rows):
+    idx = torch.from_numpy(rows).to(out.device)
+    return to_f64(out[idx[:, 0], idx[:, 2], idx[:, 1]])
+
+
+def check_any_size_properties(out, v):
+    """Outputs are convex combinations of V rows: finite and within V's range."""
+    assert torch.isfinite(out).all()
+    vmax = v.float().abs().amax().item()
+    assert out.float().abs().amax().item() <= vmax * (1 + 2 ** -7)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["wan1.3b", "wan14b", "720p16"])
+def test_queue_workload_sampled_parity(name):
+    w = configs.WORKLOADS[name]
+    say("case workload", name, w)
+    q, k, v = synth.queue_inputs(w.n, w.L, w.H, w.D, w.seed, device=DEV, k_rho=w.k_rho,
+                                 v_rho=w.v_rho)
+    cache = synth.build_cache(k, v)
+    torch.cuda.synchronize()
+    out = run_queue(q, k, v, cache, w.scale)
+    check_any_size_properties(out, v)
+    rng = np.random.default_rng(w.seed)
+    rows = sample_rows(w.n, w.L, w.H, rng)
+    ref = queue_rows_oracle(q, k, v, cache, rows, w.scale)
+    s = assert_parity(gather_rows(out, rows), ref, name)
+    say(name, "sampled rows", len(rows), s)
+    # the in-place predecessor form gives the same bits
+    out2 = run_queue(q, k, v, None, w.scale)
+    assert torch.equal(out, out2)
+    del out2, cache
+    if w.n_text:
+        qx = synth.cross_queries(w.n, w.L, w.H, w.D, w.seed, DEV)
+        kt, vt = synth.text_inputs(w.n_text, w.H, w.D, w.seed, DEV)
+        ox = ca.full(qx, kt, vt, scale=w.scale)
+        torch.cuda.synchronize()
+        check_any_size_properties(ox, vt)
+        xrows = sample_rows(w.n, w.L, w.H, rng, per=8)
+        refx = oracle.full_rows(qx[np.unique(xrows[:, 0])].cpu(), kt.cpu(), vt.cpu(),
+                                _remap_batches(xrows), w.scale)
+        sx = assert_parity(gather_rows(ox, xrows), refx, name + " cross")
+        say(name, "cross sampled rows", len(xrows), sx)
+
+
+def _remap_batches(rows):
+    uniq = np.unique(rows[:, 0])
+    r = rows.copy()
+    r[:, 0] = np.searchsorted(uniq, rows[:, 0])
+    return r
+
+
+@pytest.mark.slow
+def test_full_sequence_workload_sampled_parity():
+    w = configs.WORKLOADS["full32k"]
+    say("case workload", w.name, w)
+    q = synth.normal((1, w.L, w.H, w.D), w.seed, synth.Q_ID, DEV)
+    k = synth.normal((1, w.lkv, w.H, w.D), w.seed, synth.K_ID, DEV)
+    v = synth.normal((1, w.lkv, w.H, w.D), w.seed, synth.V_ID, DEV)
+    out = ca.full(q, k, v, scale=w.scale)
+    torch.cuda.synchronize()
+    check_any_size_properties(out, v)
+    rows = sample_rows(1, w.L, w.H, np.random.default_rng(3), per=40)
+    ref = oracle.full_rows(q.cpu(), k.cpu(), v.cpu(), rows, w.scale)
+    s = assert_parity(gather_rows(out, rows), ref, "full32k")
+    say("full32k sampled rows", len(rows), s)

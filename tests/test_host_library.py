@@ -1,0 +1,177 @@
+"""Device-free tests of the C-ABI library: symbols, validation, launch plan.
+
+No compute call is made here (there may be no GPU); the plan and the argument
+checks have device-free entry points.  The plan is compared bit for bit with
+the oracle's integer index map of each chunk's key/value set.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from chunked_spatio_temporal_amd import chunkattn as ca
+
+lib = ca.load_library()
+
+
+def test_every_declared_symbol_is_exported():
+    names = ca.declared_symbols()
+    assert "chunkattn_queue_step" in names and "chunkattn_full" in names
+    assert "chunkattn_create" in names
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in include/chunkattn.h but not exported"
+
+
+def test_library_has_no_oracle_dependency():
+    # the product library must not link or embed the oracle
+    blob = open(ca.LIB_PATH, "rb").read()
+    assert b"oracle_" not in blob
+    assert b"liboracle" not in blob
+
+
+def test_status_strings():
+    for code in range(6):
+        assert lib.chunkattn_status_string(code)
+    assert lib.chunkattn_status_string(99) == b"unknown status"
+
+
+# ---------------------------------------------------------------- validation
+
+P = 1 << 20  # a fake 16-byte-aligned device address (never dereferenced)
+
+
+def vq(**kw):
+    a = dict(q=P, k=2 * P, v=3 * P, cache=None, out=4 * P, L=16, n=2, H=2, D=128,
+             scale=0.1, dtype=ca.BF16)
+    a.update(kw)
+    return ca.validate_queue_step(a["q"], a["k"], a["v"], a["cache"], a["out"], a["L"], a["n"],
+                                  a["H"], a["D"], a["scale"], a["dtype"])
+
+
+def test_validate_queue_ok_and_empty():
+    assert vq()[0] == ca.OK
+    assert vq(cache=8 * P)[0] == ca.OK
+    assert vq(D=64, dtype=ca.F32)[0] == ca.OK
+    # empty problems are no-ops, pointers unused
+    assert vq(n=0, q=None, k=None, v=None, out=None)[0] == ca.OK
+    assert vq(L=0, q=None, k=None, v=None, out=None)[0] == ca.OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=-1), ca.EINVAL),
+    (dict(n=-3), ca.EINVAL),
+    (dict(H=0), ca.EINVAL),
+    (dict(D=96), ca.EUNSUPPORTED),
+    (dict(D=256), ca.EUNSUPPORTED),
+    (dict(dtype=7), ca.EUNSUPPORTED),
+    (dict(scale=-0.5), ca.EINVAL),
+    (dict(scale=float("nan")), ca.EINVAL),
+    (dict(scale=float("inf")), ca.EINVAL),
+    (dict(q=None), ca.EINVAL),
+    (dict(out=None), ca.EINVAL),
+    (dict(k=P + 2), ca.EINVAL),               # misaligned
+    (dict(cache=8 * P + 8), ca.EINVAL),       # misaligned cache
+    (dict(out=P), ca.EINVAL),                 # out aliases q
+    (dict(out=2 * P + 64), ca.EINVAL),        # out overlaps k
+    (dict(L=1 << 30, n=1 << 20, H=64), ca.EINVAL),  # 2^63 elements: offset overflow
+])
+def test_validate_queue_rejects(kw, code):
+    rc, msg = vq(**kw)
+    assert rc == code, msg
+    assert msg
+
+
+def vf(**kw):
+    a = dict(q=P, k=2 * P, v=3 * P, out=4 * P, B=2, lq=16, lkv=8, stride=0, H=2, D=128,
+             scale=0.1, dtype=ca.BF16)
+    a.update(kw)
+    return ca.validate_full(a["q"], a["k"], a["v"], a["out"], a["B"], a["lq"], a["lkv"],
+                            a["stride"], a["H"], a["D"], a["scale"], a["dtype"])
+
+
+def test_validate_full():
+    assert vf()[0] == ca.OK
+    assert vf(stride=8 * 2 * 128)[0] == ca.OK
+    assert vf(B=0, q=None, k=None, v=None, out=None)[0] == ca.OK
+    assert vf(lkv=0)[0] == ca.EINVAL           # attention over no keys
+    assert vf(stride=-1)[0] == ca.EINVAL
+    assert vf(stride=3)[0] == ca.EINVAL        # 6-byte stride breaks alignment
+    assert vf(D=32)[0] == ca.EUNSUPPORTED
+    assert vf(out=3 * P)[0] == ca.EINVAL
+
+
+def test_queue_step_without_context_is_rejected():
+    assert lib.chunkattn_queue_step(None, P, 2 * P, 3 * P, None, 4 * P, 16, 2, 2, 128,
+                                    ctypes.c_float(0.1), 0, None) == ca.EINVAL
+
+
+# ---------------------------------------------------------------------- plan
+
+def _slot_to_work_reference(n, n_xcd):
+    """Die x runs work items [start_x, start_x + count_x) in launch order."""
+    order = np.empty(n, np.int64)
+    per, extra = divmod(n, n_xcd)
+    start = 0
+    for x in range(n_xcd):
+        count = per + (1 if x < extra else 0)
+        slots = np.arange(x, n, n_xcd)[:count]
+        order[slots] = np.arange(start, start + count)
+        start += count
+    return order
+
+
+@pytest.mark.parametrize("L,n,H,xcd", [(128, 4, 2, 8), (6240, 8, 12, 8), (97, 5, 3, 8),
+                                       (1, 1, 1, 8), (300, 3, 7, 1), (6240, 8, 40, 8),
+                                       (14400, 16, 40, 8), (200, 2, 3, 3)])
+def test_plan_matches_oracle_index_map(L, n, H, xcd):
+    items = ca.plan_debug(L, n, H, xcd)
+    bm = ca.block_rows()
+    nq = -(-L // bm)
+    assert items.shape == (n * H * nq, 7)
+    # every (chunk, head, query row) exactly once
+    c, h, q0, qr, pc, pr, orows = items.T.astype(np.int64)
+    assert ((qr > 0) & (qr <= bm) & (q0 % bm == 0)).all()
+    key = (c * H + h) * nq + q0 // bm
+    assert sorted(key.tolist()) == list(range(n * H * nq))
+    np.testing.assert_array_equal(qr, np.minimum(bm, L - q0))
+    # each item's key/value set is the oracle's index map of its chunk, bit for bit
+    for cc in range(n):
+        sel = c == cc
+        kv = np.unique(items[sel][:, 4:7], axis=0)
+        assert kv.shape == (1, 3), "items of one chunk disagree on their key/value set"
+        pcc, prr, oww = kv[0]
+        src, ch, row = oracle.index_map(L, n, cc)
+        plan_src = np.r_[np.full(prr, oracle.SRC_PRED), np.full(oww, oracle.SRC_OWN)]
+        plan_ch = np.r_[np.full(prr, pcc), np.full(oww, cc)]
+        plan_row = np.r_[np.arange(prr), np.arange(oww)]
+        np.testing.assert_array_equal(plan_src, src)
+        np.testing.assert_array_equal(plan_ch, ch)
+        np.testing.assert_array_equal(plan_row, row)
+
+
+def test_plan_order_longest_first_and_die_ranges():
+    L, n, H, xcd = 6240, 8, 12, 8
+    items = ca.plan_debug(L, n, H, xcd)
+    nq = -(-L // ca.block_rows())
+    # reconstruct the work index of every slot and check it is the reference bijection
+    order = _slot_to_work_reference(len(items), xcd)
+    by_work = items[np.argsort(order)]
+    # work order: chunks 1..n-1 (two segments) first, chunk 0 last; t fastest
+    expect_c = np.r_[np.repeat(np.arange(1, n), H * nq), np.zeros(H * nq, int)]
+    np.testing.assert_array_equal(by_work[:, 0], expect_c)
+    np.testing.assert_array_equal(by_work[:, 1], np.tile(np.repeat(np.arange(H), nq), n))
+    np.testing.assert_array_equal(by_work[:, 2], np.tile(np.arange(nq) * ca.block_rows(), n * H))
+
+
+@pytest.mark.parametrize("n_items,xcd", [(1, 8), (7, 8), (8, 8), (9, 8), (4704, 8),
+                                         (15680, 8), (1000, 3), (5, 1)])
+def test_slot_to_work_is_a_bijection(n_items, xcd):
+    # use a plan with one chunk, one head so n_items == number of query tiles
+    bm = ca.block_rows()
+    items = ca.plan_debug(bm * n_items, 1, 1, xcd)
+    assert len(items) == n_items
+    got = items[:, 2] // bm                      # tile index == work index here
+    np.testing.assert_array_equal(got, _slot_to_work_reference(n_items, xcd))
+    assert sorted(got.tolist()) == list(range(n_items))

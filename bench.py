@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block-rows", type=int, default=0, choices=(0, 128, 256),
+                    help="query rows per work item (0: library default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -92,17 +94,22 @@ def main():
           flush=True)
 
     stream = torch.cuda.current_stream(dev)
+    flags = {0: 0, 128: ca.FLAG_BLOCK128, 256: ca.FLAG_BLOCK256}[args.block_rows]
+    ctx = ca.create(0, flags)
 
     def dominant():
         if w.kind == "queue":
-            ca.queue_step(q, k, v, cache, out=out, scale=w.scale, stream=stream)
+            ca.queue_step(q, k, v, cache, out=out, scale=w.scale, stream=stream, ctx=ctx)
         else:
-            ca.full(q, k, v, out=out, scale=w.scale, stream=stream)
+            ca.full(q, k, v, out=out, scale=w.scale, stream=stream, ctx=ctx)
+
+    def cross():
+        ca.full(qx, kt, vt, out=ox, scale=w.scale, stream=stream, ctx=ctx)
 
     def step():
         dominant()
         if w.kind == "queue" and w.n_text:
-            ca.full(qx, kt, vt, out=ox, scale=w.scale, stream=stream)
+            cross()
 
     for _ in range(args.warmup):
         step()
@@ -120,7 +127,7 @@ def main():
         dominant()
         ev[i][1].record(stream)
         if w.kind == "queue" and w.n_text:
-            ca.full(qx, kt, vt, out=ox, scale=w.scale, stream=stream)
+            cross()
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
@@ -140,7 +147,7 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
         "traffic": None,
-        "kernel": "chunk_attn_fwd<128,bf16>",
+        "kernel": f"chunk_attn_fwd<{w.D},{w.dtype},{ctx.block_rows // 32}>",
         "launch_ms_avg": round(dom_avg_ms, 4),
         "launch_ms_min": round(float(launch_ms.min()), 4),
         "launch_ms_p90": round(float(np.percentile(launch_ms, 90)), 4),
@@ -186,6 +193,7 @@ def main():
             "lkv": w.lkv if w.kind == "full" else None,
             "kv_cache": "separate buffer" if cache is not None else None,
             "text_tokens": w.n_text or None,
+            "block_rows": ctx.block_rows,
             "flops_per_step": flops_step,
         },
         "queue_steps_per_s": round(1e3 / ms_per_step, 3),

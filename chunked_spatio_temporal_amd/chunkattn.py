@@ -19,6 +19,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "chunkattn.h")
 
 OK, EINVAL, EUNSUPPORTED, EDEVICE, ENOMEM, ELAUNCH = range(6)
 BF16, F32 = 0, 1
+FLAG_BLOCK128, FLAG_BLOCK256 = 1, 2
 PLAN_FIELDS = ("chunk", "head", "q_row0", "q_rows", "pred_chunk", "pred_rows", "own_rows")
 
 
@@ -46,6 +47,8 @@ def load_library():
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float
     lib.chunkattn_block_rows.restype = i32
+    lib.chunkattn_ctx_block_rows.restype = i32
+    lib.chunkattn_ctx_block_rows.argtypes = [vp]
     lib.chunkattn_create.restype = i32
     lib.chunkattn_create.argtypes = [ctypes.POINTER(vp), i32, ctypes.c_uint]
     lib.chunkattn_destroy.restype = i32
@@ -63,7 +66,7 @@ def load_library():
     lib.chunkattn_last_error.restype = ctypes.c_char_p
     lib.chunkattn_last_error.argtypes = [vp]
     lib.chunkattn_plan_debug.restype = i32
-    lib.chunkattn_plan_debug.argtypes = [i32, i32, i32, i32, vp, i64, ctypes.POINTER(i64)]
+    lib.chunkattn_plan_debug.argtypes = [i32, i32, i32, i32, i32, vp, i64, ctypes.POINTER(i64)]
     lib.chunkattn_plan_device.restype = i32
     lib.chunkattn_plan_device.argtypes = [vp, i32, i32, i32, vp, i64, vp]
     lib.chunkattn_ctx_xcd_count.restype = i32
@@ -90,14 +93,15 @@ def block_rows() -> int:
 
 
 class Context:
-    """Owns a chunkattn_ctx bound to one device."""
+    """Owns a chunkattn_ctx bound to one device (flags: FLAG_BLOCK128/256 or 0)."""
 
-    def __init__(self, device: int = 0):
+    def __init__(self, device: int = 0, flags: int = 0):
         lib = load_library()
         h = ctypes.c_void_p()
-        _check(lib.chunkattn_create(ctypes.byref(h), int(device), 0))
+        _check(lib.chunkattn_create(ctypes.byref(h), int(device), int(flags)))
         self.handle = h
         self.device = int(device)
+        self.flags = int(flags)
 
     def close(self):
         if getattr(self, "handle", None):
@@ -114,15 +118,20 @@ class Context:
     def xcd_count(self) -> int:
         return int(load_library().chunkattn_ctx_xcd_count(self.handle))
 
+    @property
+    def block_rows(self) -> int:
+        return int(load_library().chunkattn_ctx_block_rows(self.handle))
 
-_contexts: dict[int, Context] = {}
+
+_contexts: dict[tuple, Context] = {}
 
 
-def create(device: int = 0) -> Context:
-    """The process-wide context of `device` (created on first use)."""
-    ctx = _contexts.get(device)
+def create(device: int = 0, flags: int = 0) -> Context:
+    """The process-wide context of (`device`, `flags`), created on first use."""
+    key = (int(device), int(flags))
+    ctx = _contexts.get(key)
     if ctx is None:
-        ctx = _contexts[device] = Context(device)
+        ctx = _contexts[key] = Context(device, flags)
     return ctx
 
 
@@ -155,7 +164,7 @@ def _require(t, name, dev):
         raise ValueError(f"chunkattn: {name} must be contiguous")
 
 
-def queue_step(q, k, v, kv_cache=None, out=None, scale=None, stream=None):
+def queue_step(q, k, v, kv_cache=None, out=None, scale=None, stream=None, ctx=None):
     """One queue step: chunk c attends over [predecessor K/V ; own K/V].
 
     q, k, v: [n_chunks, chunk_len, heads, head_dim] bf16/fp32 GPU tensors.
@@ -182,7 +191,7 @@ def queue_step(q, k, v, kv_cache=None, out=None, scale=None, stream=None):
         if out.shape != q.shape or out.dtype != q.dtype:
             raise ValueError("chunkattn.queue_step: out must match q")
     scale = D ** -0.5 if scale is None else float(scale)
-    ctx = create(q.device.index or 0)
+    ctx = ctx or create(q.device.index or 0)
     rc = load_library().chunkattn_queue_step(
         ctx.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_cache), _ptr(out), L, n, H, D, scale,
         _dtype_code(q), _stream(q, stream))
@@ -190,7 +199,7 @@ def queue_step(q, k, v, kv_cache=None, out=None, scale=None, stream=None):
     return out
 
 
-def full(q, k, v, out=None, scale=None, stream=None):
+def full(q, k, v, out=None, scale=None, stream=None, ctx=None):
     """Non-chunked attention of every query row over all K/V rows of its batch item.
 
     q: [batch, lq, H, D]; k, v: [batch, lkv, H, D], or [1, lkv, H, D] shared by
@@ -215,7 +224,7 @@ def full(q, k, v, out=None, scale=None, stream=None):
         if out.shape != q.shape or out.dtype != q.dtype:
             raise ValueError("chunkattn.full: out must match q")
     scale = D ** -0.5 if scale is None else float(scale)
-    ctx = create(q.device.index or 0)
+    ctx = ctx or create(q.device.index or 0)
     rc = load_library().chunkattn_full(
         ctx.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, lq, lkv, stride, H, D, scale,
         _dtype_code(q), _stream(q, stream))
@@ -223,27 +232,29 @@ def full(q, k, v, out=None, scale=None, stream=None):
     return out
 
 
-def plan_debug(chunk_len: int, n_chunks: int, heads: int, n_xcd: int = 8) -> np.ndarray:
+def plan_debug(chunk_len: int, n_chunks: int, heads: int, n_xcd: int = 8,
+               block_rows: int = 0) -> np.ndarray:
     """The queue-step launch plan computed on the host, [n_items, 7] int32."""
     lib = load_library()
     n = ctypes.c_longlong()
-    _check(lib.chunkattn_plan_debug(chunk_len, n_chunks, heads, n_xcd, None, 0, ctypes.byref(n)))
+    _check(lib.chunkattn_plan_debug(chunk_len, n_chunks, heads, n_xcd, block_rows, None, 0,
+                                    ctypes.byref(n)))
     items = np.zeros((n.value, 7), np.int32)
-    _check(lib.chunkattn_plan_debug(chunk_len, n_chunks, heads, n_xcd,
+    _check(lib.chunkattn_plan_debug(chunk_len, n_chunks, heads, n_xcd, block_rows,
                                     items.ctypes.data_as(ctypes.c_void_p), n.value,
                                     ctypes.byref(n)))
     return items
 
 
-def plan_device(chunk_len: int, n_chunks: int, heads: int, device: int = 0):
+def plan_device(chunk_len: int, n_chunks: int, heads: int, device: int = 0, ctx=None):
     """The same plan as decoded by the device kernel, [n_items, 7] int32 (GPU)."""
     import torch
     lib = load_library()
-    ctx = create(device)
+    ctx = ctx or create(device)
     n = ctypes.c_longlong()
-    _check(lib.chunkattn_plan_debug(chunk_len, n_chunks, heads, ctx.xcd_count, None, 0,
-                                    ctypes.byref(n)))
-    dev = torch.device("cuda", device)
+    _check(lib.chunkattn_plan_debug(chunk_len, n_chunks, heads, ctx.xcd_count, ctx.block_rows,
+                                    None, 0, ctypes.byref(n)))
+    dev = torch.device("cuda", ctx.device)
     items = torch.full((max(n.value, 1), 7), -7, dtype=torch.int32, device=dev)
     _check(lib.chunkattn_plan_device(ctx.handle, chunk_len, n_chunks, heads,
                                      ctypes.c_void_p(items.data_ptr()), n.value,

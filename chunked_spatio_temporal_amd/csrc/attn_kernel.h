@@ -1,28 +1,38 @@
 // gfx950 chunk-attention forward kernel.
 //
-// One workgroup (4 waves, 256 lanes) computes BM = 128 query rows of one
+// One workgroup (W = 4 or 8 waves) computes BM = 32*W query rows of one
 // (chunk, head): each wave owns 32 query rows.  Key/value rows are walked in
 // tiles of BN = 64 logical rows; a tile may straddle the predecessor/own
-// boundary, each row picking its source as it is loaded (no concatenation).
+// boundary, each row then picking its source as it is loaded, so the
+// predecessor's cached K/V is never concatenated with the chunk's own K/V
+// (feature cache, DualParal write-up section 三).
 //
 // Per tile and wave, on bf16 matrix cores (v_mfma_f32_32x32x16_bf16, fp32
 // accumulate):
-//   S^T = K . Q^T      keys on the M side, queries on N; each lane ends up
+//   S^T = K . Q^T      keys on the M side, queries on N: each lane ends up
 //                      holding 32 scores of ONE query row (its column), so the
 //                      softmax statistics of a row live in one lane pair.
-//   online softmax     running max m and sum l per query row, exp2 with
-//                      scale*log2(e) folded in; P rounded to bf16 once.
+//   online softmax     running max m and sum l per query row in the log2
+//                      domain (scale*log2(e) folded into one FMA before exp2);
+//                      m is only raised when a tile's maximum exceeds it by
+//                      more than 2^8, which is exact (O and l share m) and
+//                      skips almost every rescale of O.  P is rounded to bf16
+//                      once and l is summed from the rounded P.
 //   O^T += V^T . P^T   P^T comes straight out of the S^T accumulators as the
-//                      B operand; V^T is read from an LDS copy stored
-//                      transposed.  O^T is again one query row per lane column,
-//                      so the rescale by exp(m_old - m_new) is a per-lane scalar.
+//                      B operand; V^T is read from row-major V in LDS with the
+//                      transposing LDS read (ds_read_b64_tr_b16).  O^T again
+//                      has one query row per lane column, so any rescale is a
+//                      per-lane scalar.
 //
-// Data movement.  K and V tiles go global -> registers (128-bit loads, issued
-// one tile ahead) -> LDS (double buffered, one barrier per tile).  K is kept
-// row-major with a 16-byte-block XOR swizzle; V is transposed in registers
-// (4 keys x 8 dims per lane) and stored as V^T rows of 64 keys with a key
-// order matching the lanes' score layout, also XOR-swizzled.  Q stays in
-// registers for the whole walk.
+// Data movement.  K and V tiles are stored row-major in LDS, double
+// buffered, one barrier per tile.  bf16 tiles go straight from global memory
+// to LDS (global_load_lds_dwordx4, 16 bytes per lane, no VGPR staging): each
+// wave instruction fills 1 KB of LDS in lane order, and the lane -> global
+// address map realises a 16-byte-block XOR swizzle.  Tiles inside one segment
+// use a wave-uniform base address plus a fixed per-lane 32-bit offset; only
+// the tile that straddles the predecessor/own boundary and the ragged last
+// tile compute per-lane row addresses.  fp32 inputs are converted to bf16 in
+// registers on the way (same LDS layout).  Q stays in registers throughout.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,11 +48,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kBM = 128;  // query rows per workgroup
-constexpr int kBN = 64;   // key/value rows per tile
+#define CA_LDS __attribute__((address_space(3)))
+
+constexpr int kBN = 64;               // key/value rows per tile
+constexpr float kRescaleLog2 = 8.0f;  // raise m when the tile max exceeds it by > 2^8
 
 struct KernelArgs {
   Plan plan;
@@ -56,7 +67,7 @@ struct KernelArgs {
   int64_t kv_bstride;
   int64_t p_bstride;
   int pred_shift;
-  int row_stride;     // heads * head_dim
+  int row_stride;     // heads * head_dim (elements between consecutive tokens)
   float scale_log2;   // scale * log2(e)
 };
 
@@ -94,37 +105,75 @@ struct Io<float> {
   }
 };
 
-// ---- LDS addressing -------------------------------------------------------
-// K tile: kBN rows of D bf16 (D/8 blocks of 16 bytes), block index XOR (row & 7).
+// ---- tile geometry and LDS swizzles ----------------------------------------
 template <int D>
-__device__ __forceinline__ uint32_t k_lds_off(int row, int blk) {
-  return (uint32_t)(row * (D * 2) + ((blk ^ (row & 7)) << 4));
-}
-// V^T tile: D rows of kBN = 64 keys (8 blocks of 16 bytes).  Within each group
-// of 16 keys the stored order is [0-3, 8-11, 4-7, 12-15] so that a lane half
-// finds the 8 keys it multiplies in one block; blocks XOR-swizzled by row.
-__device__ __forceinline__ int vt_swz(int d) { return (d + (d >> 3)) & 7; }
-__device__ __forceinline__ uint32_t vt_lds_off(int d, int blk) {
-  return (uint32_t)(d * (kBN * 2) + ((blk ^ vt_swz(d)) << 4));
-}
-
-template <int D>
-struct Tile {
-  static constexpr int kDch = D / 8;                    // 16-byte chunks per row
-  static constexpr int kKRowsPerPass = kThreads / kDch;  // rows one pass loads
-  static constexpr int kKPasses = kBN / kKRowsPerPass;
-  static constexpr int kVBlocks = (kBN / 4) * kDch;      // 4 keys x 8 dims each
-  static constexpr uint32_t kKBytes = kBN * D * 2;
-  static constexpr uint32_t kVBytes = D * kBN * 2;
-  static constexpr uint32_t kBufBytes = kKBytes + kVBytes;
-  static_assert(kKRowsPerPass * kKPasses == kBN, "K tile split");
-  static_assert(kVBlocks <= kThreads, "V tile split");
+struct Geo {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kBlk = D / 8;                       // 16-byte blocks per row
+  static constexpr uint32_t kTileBytes = kBN * kRowBytes;  // one K or V tile
+  static constexpr uint32_t kBufBytes = 2 * kTileBytes;    // K + V
+  static constexpr int kRowsPerKB = 1024 / kRowBytes;      // rows per wave load (1 KB)
+  static constexpr int kChunks = kTileBytes / 1024;        // 1 KB chunks per tile
 };
 
-template <int D, typename T>
-__global__ __launch_bounds__(kThreads, 2) void chunk_attn_fwd(KernelArgs a) {
-  using TL = Tile<D>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+// K tile: block b of row r is stored at block b ^ (r mod kBlk), so the lanes
+// that read one block of consecutive rows hit distinct banks.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  return r & (Geo<D>::kBlk - 1);
+}
+// V tile: the transposing read takes 4 consecutive rows x 2 adjacent blocks per
+// 16 lanes (4 blocks per 32 lanes); placing consecutive rows 4 blocks apart
+// keeps those (row, block) pairs on distinct banks.
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+  return (4 * (r & 3) + ((r >> 2) & 3)) & (Geo<D>::kBlk - 1);
+}
+template <int D>
+__device__ __forceinline__ uint32_t k_off(int r, int blk) {
+  return (uint32_t)(r * Geo<D>::kRowBytes + ((blk ^ k_swz<D>(r)) << 4));
+}
+template <int D>
+__device__ __forceinline__ uint32_t v_off(int r, int blk) {
+  return (uint32_t)(r * Geo<D>::kRowBytes + ((blk ^ v_swz<D>(r)) << 4));
+}
+
+// 16 bytes per lane from global memory straight into LDS: the wave writes 1 KB
+// at `lds_chunk` (a wave-uniform address) in lane order.  The builtin exists
+// only in the device compilation pass.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_chunk) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, (CA_LDS void*)lds_chunk, 16, 0, 0);
+#endif
+}
+
+// The value held by lane (l ^ 32): the other half of the wave, which holds the
+// other 32 keys of the same query row.  (ds_bpermute; the compiler used here
+// folds the two results of a same-operand v_permlane32_swap into one, which
+// would drop the other half.)
+__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32); }
+
+// s_waitcnt vmcnt(0): every global load of this wave (including the ones that
+// write LDS directly) has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+struct NoMask {
+  static constexpr bool value = false;
+};
+template <int B>
+struct Buf {
+  static constexpr int value = B;
+};
+struct Mask {
+  static constexpr bool value = true;
+};
+
+template <int D, typename T, int W>
+__global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
+  using G = Geo<D>;
+  constexpr int kCpw = G::kChunks / W;  // 1 KB load chunks per wave per matrix
+  static_assert(kCpw * W == G::kChunks, "tile split across waves");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -134,20 +183,21 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_fwd(KernelArgs a) {
 
   const int64_t w = slot_to_work(blockIdx.x, a.plan.n_items, a.plan.n_xcd);
   const Item it = decode(a.plan, w);
-  const int total = it.pred_rows + it.own_rows;
+  const int pred = it.pred_rows;
+  const int total = pred + it.own_rows;
   const int n_tiles = (total + kBN - 1) / kBN;
+  const int64_t rs = a.row_stride;
 
   const T* qb = static_cast<const T*>(a.q) + it.b * a.q_bstride + (int64_t)it.h * D;
   const T* kown = static_cast<const T*>(a.k) + it.b * a.kv_bstride + (int64_t)it.h * D;
   const T* vown = static_cast<const T*>(a.v) + it.b * a.kv_bstride + (int64_t)it.h * D;
   const T* kpre = kown;
   const T* vpre = vown;
-  if (it.pred_rows > 0) {
+  if (pred > 0) {
     const int64_t pi = (int64_t)(it.b - a.pred_shift) * a.p_bstride + (int64_t)it.h * D;
     kpre = static_cast<const T*>(a.pk) + pi;
     vpre = static_cast<const T*>(a.pv) + pi;
   }
-  const int64_t rs = a.row_stride;
 
   // ---- Q fragment: B operand of S^T = K.Q^T, one query row per lane column
   const int qrow = it.q0 + wave * 32 + l32;
@@ -161,73 +211,70 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_fwd(KernelArgs a) {
       qf[ks] = u32x4_t{0u, 0u, 0u, 0u};
   }
 
-  // ---- per-thread load assignment for one K/V tile
-  const int k_row0 = tid / TL::kDch;
-  const int k_blk = tid % TL::kDch;
-  int v_dc = 0, v_kg = 0;
-  const bool v_loader = tid < TL::kVBlocks;
-  {
-    const int l16 = tid & 15, grp = tid >> 4;
-    int bi;
-    if (TL::kDch == 16) {
-      v_dc = (l16 & 7) + 8 * (grp & 1);
-      bi = grp >> 1;
-    } else {
-      v_dc = l16 & 7;
-      bi = grp;
-    }
-    v_kg = ((bi >> 1) << 2) + (bi & 1) + 2 * (l16 >> 3);
+  // ---- per-lane load map: LDS chunk c = wave*kCpw + i receives, at byte
+  // c*1024 + lane*16, tile row r = c*kRowsPerKB + lane/kBlk and physical block
+  // lane%kBlk, i.e. logical block (lane%kBlk) ^ swizzle(r).
+  int lrow[kCpw];
+  uint32_t koffs[kCpw], voffs[kCpw];  // element offsets within a one-segment tile
+#pragma unroll
+  for (int i = 0; i < kCpw; ++i) {
+    const int c = wave * kCpw + i;
+    const int r = c * G::kRowsPerKB + lane / G::kBlk;
+    const int pb = lane % G::kBlk;
+    lrow[i] = r;
+    koffs[i] = (uint32_t)(r * rs + ((pb ^ k_swz<D>(r)) * 8));
+    voffs[i] = (uint32_t)(r * rs + ((pb ^ v_swz<D>(r)) * 8));
   }
 
-  u32x4_t kreg[TL::kKPasses];
-  u32x4_t vreg[4];
-
-  auto row_ptr = [&](const T* pre, const T* own, int j) -> const T* {
-    return j < it.pred_rows ? pre + j * rs : own + (j - it.pred_rows) * rs;
-  };
-
-  auto load_tile = [&](int t) {
-    const int base = t * kBN;
+  // Issues the loads of tile t into LDS buffer `buf`.
+  auto load_tile = [&](int t, int buf) {
+    unsigned char* kb = smem + buf * G::kBufBytes;
+    unsigned char* vb = kb + G::kTileBytes;
+    const int r0 = t * kBN;
+    if constexpr (sizeof(T) == 2) {
+      if (r0 + kBN <= pred || (r0 >= pred && r0 + kBN <= total)) {
+        // whole tile in one segment: uniform base + fixed per-lane offsets
+        const bool in_pred = r0 + kBN <= pred;
+        const int64_t row = in_pred ? r0 : r0 - pred;
+        const T* kbase = (in_pred ? kpre : kown) + row * rs;
+        const T* vbase = (in_pred ? vpre : vown) + row * rs;
 #pragma unroll
-    for (int i = 0; i < TL::kKPasses; ++i) {
-      const int j = base + k_row0 + i * TL::kKRowsPerPass;
-      if (j < total)
-        kreg[i] = Io<T>::load8(row_ptr(kpre, kown, j) + k_blk * 8);
-      else
-        kreg[i] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-    if (v_loader) {
+        for (int i = 0; i < kCpw; ++i) {
+          const int c = wave * kCpw + i;
+          load_lds16(kbase + koffs[i], kb + c * 1024);
+          load_lds16(vbase + voffs[i], vb + c * 1024);
+        }
+      } else {
+        // straddling or ragged tile: per-lane row select; rows past the end
+        // re-read the last row (their scores are masked, their P is zero)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = base + v_kg * 4 + i;
-        if (j < total)
-          vreg[i] = Io<T>::load8(row_ptr(vpre, vown, j) + v_dc * 8);
-        else
-          vreg[i] = u32x4_t{0u, 0u, 0u, 0u};
+        for (int i = 0; i < kCpw; ++i) {
+          const int c = wave * kCpw + i;
+          int j = r0 + lrow[i];
+          j = j < total ? j : total - 1;
+          const int pb = lane % G::kBlk;
+          const int kblk = pb ^ k_swz<D>(lrow[i]);
+          const int vblk = pb ^ v_swz<D>(lrow[i]);
+          const T* kr = j < pred ? kpre + j * rs : kown + (j - pred) * rs;
+          const T* vr = j < pred ? vpre + j * rs : vown + (j - pred) * rs;
+          load_lds16(kr + kblk * 8, kb + c * 1024);
+          load_lds16(vr + vblk * 8, vb + c * 1024);
+        }
       }
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-    unsigned char* kb = smem + buf * TL::kBufBytes;
-    unsigned char* vb = kb + TL::kKBytes;
+    } else {
+      // fp32 storage: convert to bf16 in registers, store with the same layout
 #pragma unroll
-    for (int i = 0; i < TL::kKPasses; ++i) {
-      const int r = k_row0 + i * TL::kKRowsPerPass;
-      *reinterpret_cast<u32x4_t*>(kb + k_lds_off<D>(r, k_blk)) = kreg[i];
-    }
-    if (v_loader) {
-      // 4 keys x 8 dims -> for each dim, the 4 keys as two packed pairs
-      const int blk = 2 * (v_kg >> 2) + (v_kg & 1);
-      const int half = (v_kg & 3) >> 1;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t e0 = vreg[0][m], e1 = vreg[1][m], e2 = vreg[2][m], e3 = vreg[3][m];
-        const u32x2_t even = {(e0 & 0xffffu) | (e1 << 16), (e2 & 0xffffu) | (e3 << 16)};
-        const u32x2_t odd = {(e0 >> 16) | (e1 & 0xffff0000u), (e2 >> 16) | (e3 & 0xffff0000u)};
-        const int d0 = v_dc * 8 + 2 * m;
-        *reinterpret_cast<u32x2_t*>(vb + vt_lds_off(d0, blk) + half * 8) = even;
-        *reinterpret_cast<u32x2_t*>(vb + vt_lds_off(d0 + 1, blk) + half * 8) = odd;
+      for (int i = 0; i < kCpw; ++i) {
+        const int c = wave * kCpw + i;
+        int j = r0 + lrow[i];
+        j = j < total ? j : total - 1;
+        const int pb = lane % G::kBlk;
+        const T* kr = j < pred ? kpre + j * rs : kown + (j - pred) * rs;
+        const T* vr = j < pred ? vpre + j * rs : vown + (j - pred) * rs;
+        const u32x4_t kv = Io<T>::load8(kr + (pb ^ k_swz<D>(lrow[i])) * 8);
+        const u32x4_t vv = Io<T>::load8(vr + (pb ^ v_swz<D>(lrow[i])) * 8);
+        *reinterpret_cast<u32x4_t*>(kb + c * 1024 + lane * 16) = kv;
+        *reinterpret_cast<u32x4_t*>(vb + c * 1024 + lane * 16) = vv;
       }
     }
   };
@@ -237,42 +284,68 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_fwd(KernelArgs a) {
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
+  float m_run = -__builtin_inff();  // running max, log2 domain (score * scale * log2 e)
+  float l_run = 0.f;                // this lane half's share of the softmax denominator
   const float s2 = a.scale_log2;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // Per-lane LDS byte offsets; everything else in an address is an immediate.
+  // K read for k-step ks and key block kb2: row 32*kb2 + l32, logical block
+  // 2*ks + hh.  With x = l32 & (kBlk-1) the swizzled block is
+  // 2*(ks ^ (x>>1)) + (hh ^ (x&1)), so only ks ^ (x>>1) varies per lane.
+  constexpr int kKs = D / 16;
+  uint32_t koff_lds[kKs];
+  {
+    const int x = l32 & (G::kBlk - 1);
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks)
+      koff_lds[ks] = (uint32_t)(l32 * G::kRowBytes +
+                                ((2 * (ks ^ (x >> 1)) + (hh ^ (x & 1))) << 4));
+  }
+  // V transposing reads for d-block db and lo/hi half w: row 16s + 4hh + j/4 + 8w
+  // (s only shifts the row by 16, which leaves the swizzle unchanged), column
+  // block 4db + 2g1 + (j&3)/2, 8-byte half j&1.
+  constexpr int kDb = D / 32;
+  uint32_t voff_lds[kDb][2];
+  {
+    const int g1 = (lane >> 4) & 1;
+    const int j16 = lane & 15;
+#pragma unroll
+    for (int db = 0; db < kDb; ++db)
+#pragma unroll
+      for (int w2 = 0; w2 < 2; ++w2) {
+        const int r = 4 * hh + (j16 >> 2) + 8 * w2;
+        const int col = 32 * db + 16 * g1 + 4 * (j16 & 3);
+        voff_lds[db][w2] = v_off<D>(r, col >> 3) + ((col >> 2) & 1) * 8;
+      }
+  }
+  CA_LDS unsigned char* lds = (CA_LDS unsigned char*)smem;
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const bool has_next = t + 1 < n_tiles;
-    if (has_next) load_tile(t + 1);
+  // One tile: S^T, online softmax, O^T update.  kBuf: LDS buffer (compile-time
+  // so that it folds into the immediate offsets).  Mask: keys >= total are out.
+  auto compute = [&](int t, auto buf_tag, auto mask_tag) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    constexpr uint32_t kKBase = decltype(buf_tag)::value * G::kBufBytes;
+    constexpr uint32_t kVBase = kKBase + G::kTileBytes;
 
-    const unsigned char* kb = smem + (t & 1) * TL::kBufBytes;
-    const unsigned char* vb = kb + TL::kKBytes;
-
-    // S^T = K . Q^T for two blocks of 32 keys
     f32x16_t sacc[kBN / 32];
 #pragma unroll
     for (int kb2 = 0; kb2 < kBN / 32; ++kb2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kb2][i] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < kKs; ++ks) {
 #pragma unroll
       for (int kb2 = 0; kb2 < kBN / 32; ++kb2) {
-        const u32x4_t kv =
-            *reinterpret_cast<const u32x4_t*>(kb + k_lds_off<D>(kb2 * 32 + l32, 2 * ks + hh));
+        const u32x4_t kv = *(CA_LDS const u32x4_t*)(lds + koff_lds[ks] +
+                                                   (kKBase + kb2 * 32 * G::kRowBytes));
         sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8_t, kv), __builtin_bit_cast(bf16x8_t, qf[ks]), sacc[kb2],
             0, 0, 0);
       }
     }
 
-    // keys past the end of R_c (last tile only) take no part
-    const bool ragged = (t + 1) * kBN > total;
-    if (ragged) {
+    if constexpr (kMask) {
 #pragma unroll
       for (int kb2 = 0; kb2 < kBN / 32; ++kb2)
 #pragma unroll
@@ -282,66 +355,103 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_attn_fwd(KernelArgs a) {
         }
     }
 
-    // online softmax for this lane's query row
+    // tile max of this lane's query row, then across the two lane halves
     float mx = sacc[0][0];
 #pragma unroll
     for (int kb2 = 0; kb2 < kBN / 32; ++kb2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb2][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    // first tile: nothing to rescale (also keeps scale = 0 free of inf*0)
-    const float alpha =
-        m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * s2);
-    m_run = m_new;
-    const float msc = m_new * s2;
+    mx = fmaxf(mx, other_half(mx));
+    const float mxs = mx * s2;
+    if (__builtin_amdgcn_ballot_w64(mxs > m_run + kRescaleLog2) != 0) {
+      const float m_new = fmaxf(m_run, mxs);
+      const float alpha =
+          m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDb; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
 
     uint32_t pk[kBN / 32][8];
-    float psum = 0.f;
 #pragma unroll
     for (int kb2 = 0; kb2 < kBN / 32; ++kb2) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][2 * i], s2, -msc));
-        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][2 * i + 1], s2, -msc));
-        if (ragged) {
+        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][2 * i], s2, -m_run));
+        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][2 * i + 1], s2, -m_run));
+        if constexpr (kMask) {
           const int key0 = t * kBN + kb2 * 32 + 8 * ((2 * i) >> 2) + 4 * hh + ((2 * i) & 3);
           if (key0 >= total) p0 = 0.f;
           if (key0 + 1 >= total) p1 = 0.f;
         }
         pk[kb2][i] = pack_bf16(p0, p1);
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[kb2][i]),
-                                               bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, psum,
-                                               false);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[kb2][i]), ones,
+                                                l_run, false);
       }
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
 
-    // O^T += V^T . P^T, 16 keys per step
+    // O^T += V^T . P^T, 16 keys per step.  Lane (group g = lane/16, j = lane%16)
+    // addresses row 16s + 4hh + j/4 (and +8), columns 32db + 16(g&1) + 4(j&3)..+3;
+    // the transposing read hands lane j those 4 rows at its own column
+    // 32db + 16(g&1) + j, which are the keys its P^T operand holds.
 #pragma unroll
     for (int s = 0; s < kBN / 16; ++s) {
       const u32x4_t pb = {pk[s >> 1][(s & 1) * 4 + 0], pk[s >> 1][(s & 1) * 4 + 1],
                           pk[s >> 1][(s & 1) * 4 + 2], pk[s >> 1][(s & 1) * 4 + 3]};
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const u32x4_t vv =
-            *reinterpret_cast<const u32x4_t*>(vb + vt_lds_off(db * 32 + l32, 2 * s + hh));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv),
+      for (int db = 0; db < kDb; ++db) {
+        const uint32_t imm = kVBase + 16 * s * G::kRowBytes;
+        const i16x4_t lo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((CA_LDS i16x4_t*)(lds + voff_lds[db][0] + imm));
+        const i16x4_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((CA_LDS i16x4_t*)(lds + voff_lds[db][1] + imm));
+        const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
+        const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
+        const u32x4_t va = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va),
                                                            __builtin_bit_cast(bf16x8_t, pb),
                                                            oacc[db], 0, 0, 0);
       }
     }
+  };
 
-    if (has_next) store_tile((t + 1) & 1);
+  // One pipeline step: start loading tile t+1 into the other buffer, compute
+  // tile t, then wait for the loads and synchronise the workgroup.
+  auto step = [&](int t, auto buf_tag, auto mask_tag) {
+    constexpr int kB = decltype(buf_tag)::value;
+    if (t + 1 < n_tiles) load_tile(t + 1, kB ^ 1);
+    compute(t, buf_tag, mask_tag);
+    wait_vmem();
     __syncthreads();
+  };
+
+  load_tile(0, 0);
+  wait_vmem();
+  __syncthreads();
+  // full tiles in pairs (buffer 0, buffer 1), so the buffer is a constant
+  const int n_full = total / kBN;
+  int t = 0;
+  for (; t + 2 <= n_full; t += 2) {
+    step(t, Buf<0>{}, NoMask{});
+    step(t + 1, Buf<1>{}, NoMask{});
+  }
+  if (t < n_full) {
+    step(t, Buf<0>{}, NoMask{});
+    ++t;
+  }
+  // the ragged last tile, if any
+  if (t < n_tiles) {
+    if (t & 1)
+      step(t, Buf<1>{}, Mask{});
+    else
+      step(t, Buf<0>{}, Mask{});
   }
 
   // ---- epilogue: normalise and store this lane's query row
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = l_run + other_half(l_run);
   const float inv = 1.0f / l_tot;
   if (qvalid) {
     T* ob = static_cast<T*>(a.o) + it.b * a.q_bstride + (int64_t)qrow * rs + (int64_t)it.h * D;

@@ -16,6 +16,7 @@ struct chunkattn_ctx {
   int device = 0;
   int n_cu = 0;
   int n_xcd = 1;
+  int waves = 8;  // waves per workgroup; a work item covers 32 * waves query rows
   std::string arch;
   std::string err;
 };
@@ -24,6 +25,9 @@ namespace {
 
 using chunkattn::KernelArgs;
 using chunkattn::Plan;
+
+constexpr int kDefaultWaves = 8;
+constexpr int kMinBlockRows = 128;  // smallest work item (4 waves); bounds the grid
 
 thread_local std::string g_thread_err;
 
@@ -88,7 +92,7 @@ int validate_queue(std::string* err, const void* q, const void* k, const void* v
       overlaps(out, bytes, v, bytes) || (kv_cache && overlaps(out, bytes, kv_cache, 2 * bytes)))
     return set_err(err, CHUNKATTN_EINVAL, "out overlaps an input tensor");
   const long double items =
-      (long double)n * heads * ((L + chunkattn::kBM - 1) / chunkattn::kBM);
+      (long double)n * heads * ((L + kMinBlockRows - 1) / kMinBlockRows);
   if (items > 2147483647.0L)
     return set_err(err, CHUNKATTN_EUNSUPPORTED, "too many work items for one launch");
   return CHUNKATTN_OK;
@@ -127,27 +131,50 @@ int validate_full(std::string* err, const void* q, const void* k, const void* v,
   if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kb) || overlaps(out, qb, v, kb))
     return set_err(err, CHUNKATTN_EINVAL, "out overlaps an input tensor");
   const long double items =
-      (long double)batch * heads * ((lq + chunkattn::kBM - 1) / chunkattn::kBM);
+      (long double)batch * heads * ((lq + kMinBlockRows - 1) / kMinBlockRows);
   if (items > 2147483647.0L)
     return set_err(err, CHUNKATTN_EUNSUPPORTED, "too many work items for one launch");
   return CHUNKATTN_OK;
 }
 
-template <int D, typename T>
+}  // namespace
+
+// Every kernel configuration the host can launch, instantiated explicitly.
+namespace chunkattn {
+template __global__ void chunk_attn_fwd<128, __bf16, 4>(KernelArgs);
+template __global__ void chunk_attn_fwd<128, __bf16, 8>(KernelArgs);
+template __global__ void chunk_attn_fwd<128, float, 4>(KernelArgs);
+template __global__ void chunk_attn_fwd<128, float, 8>(KernelArgs);
+template __global__ void chunk_attn_fwd<64, __bf16, 4>(KernelArgs);
+template __global__ void chunk_attn_fwd<64, __bf16, 8>(KernelArgs);
+template __global__ void chunk_attn_fwd<64, float, 4>(KernelArgs);
+template __global__ void chunk_attn_fwd<64, float, 8>(KernelArgs);
+}  // namespace chunkattn
+
+namespace {
+
+template <int D, typename T, int W>
 hipError_t launch_t(const KernelArgs& a, hipStream_t stream) {
-  using TL = chunkattn::Tile<D>;
+  using G = chunkattn::Geo<D>;
   const dim3 grid((unsigned)a.plan.n_items);
-  hipLaunchKernelGGL((chunkattn::chunk_attn_fwd<D, T>), grid, dim3(chunkattn::kThreads),
-                     2 * TL::kBufBytes, stream, a);
+  hipLaunchKernelGGL((chunkattn::chunk_attn_fwd<D, T, W>), grid, dim3(W * 64),
+                     2 * G::kBufBytes, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch(const KernelArgs& a, int head_dim, int dtype, hipStream_t stream) {
+template <int W>
+hipError_t launch_w(const KernelArgs& a, int head_dim, int dtype, hipStream_t stream) {
   if (head_dim == 128)
-    return dtype == CHUNKATTN_BF16 ? launch_t<128, __bf16>(a, stream)
-                                   : launch_t<128, float>(a, stream);
-  return dtype == CHUNKATTN_BF16 ? launch_t<64, __bf16>(a, stream)
-                                 : launch_t<64, float>(a, stream);
+    return dtype == CHUNKATTN_BF16 ? launch_t<128, __bf16, W>(a, stream)
+                                   : launch_t<128, float, W>(a, stream);
+  return dtype == CHUNKATTN_BF16 ? launch_t<64, __bf16, W>(a, stream)
+                                 : launch_t<64, float, W>(a, stream);
+}
+
+hipError_t launch(const KernelArgs& a, int waves, int head_dim, int dtype,
+                  hipStream_t stream) {
+  return waves == 4 ? launch_w<4>(a, head_dim, dtype, stream)
+                    : launch_w<8>(a, head_dim, dtype, stream);
 }
 
 // Makes the context's device current for the duration of a call.
@@ -168,7 +195,7 @@ int run(chunkattn_ctx* ctx, const KernelArgs& a, int head_dim, int dtype, void* 
   DeviceGuard g(ctx->device);
   if (!g.ok) return set_err(&ctx->err, CHUNKATTN_EDEVICE, "cannot make device %d current",
                             ctx->device);
-  const hipError_t e = launch(a, head_dim, dtype, static_cast<hipStream_t>(stream));
+  const hipError_t e = launch(a, ctx->waves, head_dim, dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return set_err(&ctx->err, CHUNKATTN_ELAUNCH, "kernel launch failed: %s",
                    hipGetErrorString(e));
@@ -180,12 +207,16 @@ int run(chunkattn_ctx* ctx, const KernelArgs& a, int head_dim, int dtype, void* 
 
 extern "C" {
 
-int chunkattn_block_rows(void) { return chunkattn::kBM; }
+int chunkattn_block_rows(void) { return 32 * kDefaultWaves; }
+
+int chunkattn_ctx_block_rows(const chunkattn_ctx* ctx) { return ctx ? 32 * ctx->waves : 0; }
 
 int chunkattn_create(chunkattn_ctx** out, int device_ordinal, unsigned flags) {
   if (!out) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "out must be non-NULL");
   *out = nullptr;
-  if (flags != 0) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "flags must be 0");
+  const unsigned known = CHUNKATTN_FLAG_BLOCK128 | CHUNKATTN_FLAG_BLOCK256;
+  if ((flags & ~known) != 0 || flags == known)
+    return set_err(&g_thread_err, CHUNKATTN_EINVAL, "unknown or conflicting flags 0x%x", flags);
   int count = 0;
   if (hipGetDeviceCount(&count) != hipSuccess || device_ordinal < 0 || device_ordinal >= count)
     return set_err(&g_thread_err, CHUNKATTN_EDEVICE, "no HIP device %d (found %d)",
@@ -200,6 +231,8 @@ int chunkattn_create(chunkattn_ctx** out, int device_ordinal, unsigned flags) {
   chunkattn_ctx* ctx = new (std::nothrow) chunkattn_ctx();
   if (!ctx) return set_err(&g_thread_err, CHUNKATTN_ENOMEM, "context allocation failed");
   ctx->device = device_ordinal;
+  ctx->waves = (flags & CHUNKATTN_FLAG_BLOCK128) ? 4 : (flags & CHUNKATTN_FLAG_BLOCK256) ? 8
+                                                                                       : kDefaultWaves;
   ctx->n_cu = prop.multiProcessorCount;
   ctx->arch = prop.gcnArchName;
   int xcc = 0;
@@ -250,7 +283,7 @@ int chunkattn_queue_step(chunkattn_ctx* ctx, const void* q, const void* k, const
   const size_t es = elem_size(dtype);
   KernelArgs a;
   a.plan = chunkattn::make_plan(n_chunks, 1, heads, chunk_len, chunk_len, chunk_len,
-                                chunkattn::kBM, ctx->n_xcd);
+                                32 * ctx->waves, ctx->n_xcd);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -285,7 +318,7 @@ int chunkattn_full(chunkattn_ctx* ctx, const void* q, const void* k, const void*
     return CHUNKATTN_OK;
   }
   KernelArgs a;
-  a.plan = chunkattn::make_plan(batch, batch, heads, lq, lkv, 0, chunkattn::kBM, ctx->n_xcd);
+  a.plan = chunkattn::make_plan(batch, batch, heads, lq, lkv, 0, 32 * ctx->waves, ctx->n_xcd);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -317,16 +350,18 @@ const char* chunkattn_last_error(const chunkattn_ctx* ctx) {
   return ctx ? ctx->err.c_str() : g_thread_err.c_str();
 }
 
-int chunkattn_plan_debug(int chunk_len, int n_chunks, int heads, int n_xcd, int* items,
-                         long long cap, long long* n_items) {
+int chunkattn_plan_debug(int chunk_len, int n_chunks, int heads, int n_xcd, int block_rows,
+                         int* items, long long cap, long long* n_items) {
   g_thread_err.clear();
   if (!n_items) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "n_items must be non-NULL");
-  if (chunk_len < 0 || n_chunks < 0 || heads < 1 || cap < 0 || (cap > 0 && !items))
+  if (block_rows == 0) block_rows = 32 * kDefaultWaves;
+  if (chunk_len < 0 || n_chunks < 0 || heads < 1 || cap < 0 || (cap > 0 && !items) ||
+      (block_rows != 128 && block_rows != 256))
     return set_err(&g_thread_err, CHUNKATTN_EINVAL, "bad plan_debug arguments");
   *n_items = 0;
   if (chunk_len == 0 || n_chunks == 0) return CHUNKATTN_OK;
   const Plan p = chunkattn::make_plan(n_chunks, 1, heads, chunk_len, chunk_len, chunk_len,
-                                      chunkattn::kBM, n_xcd);
+                                      block_rows, n_xcd);
   *n_items = p.n_items;
   for (int64_t slot = 0; slot < p.n_items && slot < cap; ++slot) {
     const chunkattn::Item it =
@@ -350,7 +385,7 @@ int chunkattn_plan_device(chunkattn_ctx* ctx, int chunk_len, int n_chunks, int h
     return set_err(&ctx->err, CHUNKATTN_EINVAL, "bad plan_device arguments");
   if (chunk_len == 0 || n_chunks == 0 || cap == 0) return CHUNKATTN_OK;
   const Plan p = chunkattn::make_plan(n_chunks, 1, heads, chunk_len, chunk_len, chunk_len,
-                                      chunkattn::kBM, ctx->n_xcd);
+                                      32 * ctx->waves, ctx->n_xcd);
   const int64_t n = p.n_items < cap ? p.n_items : cap;
   DeviceGuard g(ctx->device);
   if (!g.ok) return set_err(&ctx->err, CHUNKATTN_EDEVICE, "cannot make device current");

@@ -72,16 +72,25 @@ typedef enum {
     CHUNKATTN_F32 = 1   /* fp32 storage in and out (operands rounded to bf16) */
 } chunkattn_dtype;
 
-/* Query rows handled by one work item (one workgroup). */
+/* chunkattn_create flags: query rows per work item (one workgroup). */
+#define CHUNKATTN_FLAG_BLOCK128 1u /* 128 rows, 4 waves, two workgroups per CU */
+#define CHUNKATTN_FLAG_BLOCK256 2u /* 256 rows, 8 waves, one workgroup per CU */
+
+/* Query rows per work item of a context created with flags = 0. */
 int chunkattn_block_rows(void);
 
 /*
  * Creates a context bound to HIP device `device_ordinal`.  Fails with
  * CHUNKATTN_EUNSUPPORTED unless the device is gfx950, CHUNKATTN_EDEVICE if the
- * ordinal is invalid.  `flags` must be 0.  On success *out owns the context;
- * release it with chunkattn_destroy.
+ * ordinal is invalid.  `flags` is 0 (library default work-item size) or one of
+ * CHUNKATTN_FLAG_BLOCK128 / CHUNKATTN_FLAG_BLOCK256; results do not depend on
+ * it beyond fp32 rounding order.  On success *out owns the context; release it
+ * with chunkattn_destroy.
  */
 int chunkattn_create(chunkattn_ctx **out, int device_ordinal, unsigned flags);
+
+/* Query rows per work item of this context (128 or 256). */
+int chunkattn_ctx_block_rows(const chunkattn_ctx *ctx);
 
 /* Releases a context (NULL is accepted). */
 int chunkattn_destroy(chunkattn_ctx *ctx);
@@ -149,17 +158,19 @@ const char *chunkattn_last_error(const chunkattn_ctx *ctx);
  *   (chunk, head, q_row0, q_rows, pred_chunk, pred_rows, own_rows)
  * pred_chunk is c-1 when the chunk reads a predecessor (pred_rows = chunk_len),
  * else -1 (pred_rows = 0).  n_xcd is the number of accelerator dies the
- * workgroups are spread over (8 on MI355X; 1 disables the die-aware order).
+ * workgroups are spread over (8 on MI355X; 1 disables the die-aware order);
+ * block_rows is the work-item size (128 or 256; 0 = chunkattn_block_rows()).
  * Writes at most `cap` records to `items` (may be NULL when cap is 0) and the
  * total count to *n_items.
  */
-int chunkattn_plan_debug(int chunk_len, int n_chunks, int heads, int n_xcd, int *items,
-                         long long cap, long long *n_items);
+int chunkattn_plan_debug(int chunk_len, int n_chunks, int heads, int n_xcd, int block_rows,
+                         int *items, long long cap, long long *n_items);
 
 /*
  * The same plan as decoded on the device by the attention kernel's own decode
  * routine: writes n_items * 7 ints to device memory `dev_items` on hip_stream,
- * using the context's die count.  For bit-exact tests of the device decode.
+ * using the context's die count and work-item size.  For bit-exact tests of
+ * the device decode.
  */
 int chunkattn_plan_device(chunkattn_ctx *ctx, int chunk_len, int n_chunks, int heads,
                           int *dev_items, long long cap, void *hip_stream);

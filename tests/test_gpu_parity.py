@@ -37,22 +37,26 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_queue(q, k, v, cache=None, scale=None):
-    out = ca.queue_step(q, k, v, cache, scale=scale)
+FLAGS = [pytest.param(ca.FLAG_BLOCK256, id="bm256"), pytest.param(ca.FLAG_BLOCK128, id="bm128")]
+
+
+def run_queue(q, k, v, cache=None, scale=None, flags=0):
+    out = ca.queue_step(q, k, v, cache, scale=scale, ctx=ca.create(0, flags))
     torch.cuda.synchronize()
     return out
 
 
 # ------------------------------------------------------------------ small / exact
 
-def test_tiny_config_full_parity():
+@pytest.mark.parametrize("flags", FLAGS)
+def test_tiny_config_full_parity(flags):
     w = configs.WORKLOADS["tiny"]
-    say("case tiny", w)
+    say("case tiny", w, flags)
     q, k, v = synth.queue_inputs(w.n, w.L, w.H, w.D, w.seed, device=DEV, dtype=torch.float32)
     cache = synth.build_cache(k, v)
     ref = oracle.queue_step(q, k, v, None, scale=w.scale)
-    out_alias = run_queue(q, k, v, None, w.scale)
-    out_cache = run_queue(q, k, v, cache, w.scale)
+    out_alias = run_queue(q, k, v, None, w.scale, flags)
+    out_cache = run_queue(q, k, v, cache, w.scale, flags)
     assert out_alias.dtype == torch.float32
     s = assert_parity(to_f64(out_alias), ref, "tiny alias")
     say("tiny stats", s)
@@ -74,15 +78,16 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("flags", FLAGS)
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s[:4])) + str(s[4])[-4:])
-def test_ragged_shapes_full_parity(shape):
+def test_ragged_shapes_full_parity(shape, flags):
     n, L, H, D, dt = shape
-    say("case ragged", shape)
+    say("case ragged", shape, flags)
     q, k, v = synth.queue_inputs(n, L, H, D, seed=100 + L, device=DEV, dtype=dt, k_rho=0.9)
     cache = synth.build_cache(k, v)
     ref = oracle.queue_step(q, k, v, None)
-    a = run_queue(q, k, v, None)
-    b = run_queue(q, k, v, cache)
+    a = run_queue(q, k, v, None, flags=flags)
+    b = run_queue(q, k, v, cache, flags=flags)
     assert_parity(to_f64(a), ref, f"ragged {shape}")
     assert torch.equal(a, b), "alias and cache modes differ"
 
@@ -119,7 +124,8 @@ def test_guard_bands_and_cache_slot0_never_read():
     assert torch.equal(op, ref)
 
 
-def test_range_fingerprint_bit_exact():
+@pytest.mark.parametrize("flags", FLAGS)
+def test_range_fingerprint_bit_exact(flags):
     """Q = 0 makes every weight exactly 1, so O[c,r,h,d] = (number of tokens t
     in R_c with (t + 7h) mod D == d) / |R_c|, with t the token's global index.
     The kernel's fp32 sums of ones are exact, so the bf16 output must equal the
@@ -141,7 +147,7 @@ def test_range_fingerprint_bit_exact():
             exp[c, :, h, :] = counts / len(toks)
     exp_bf16 = torch.from_numpy(exp).float().to(torch.bfloat16)
     for cc in (None, cache):
-        out = run_queue(q, k, v, cc)
+        out = run_queue(q, k, v, cc, flags=flags)
         assert torch.equal(out.cpu(), exp_bf16), "fingerprint mismatch"
 
 
@@ -184,28 +190,40 @@ def test_errors_are_raised_not_launched():
     assert e.value.status == ca.EINVAL
 
 
-def test_device_plan_equals_host_plan():
-    ctx = ca.create(0)
-    say("xcd count", ctx.xcd_count)
+@pytest.mark.parametrize("flags", FLAGS)
+def test_device_plan_equals_host_plan(flags):
+    ctx = ca.create(0, flags)
+    say("xcd count", ctx.xcd_count, "block rows", ctx.block_rows)
     for (L, n, H) in [(128, 4, 2), (6240, 8, 40), (97, 5, 3), (14400, 16, 40)]:
-        dev = ca.plan_device(L, n, H).cpu().numpy()
-        host = ca.plan_debug(L, n, H, ctx.xcd_count)
+        dev = ca.plan_device(L, n, H, ctx=ctx).cpu().numpy()
+        host = ca.plan_debug(L, n, H, ctx.xcd_count, ctx.block_rows)
         np.testing.assert_array_equal(dev, host)
+
+
+def test_block_sizes_give_identical_bits():
+    """A wave computes the same 32 query rows the same way whichever work-item
+    size groups it, so the two launch configurations agree bit for bit."""
+    q, k, v = synth.queue_inputs(5, 700, 3, 128, seed=14, device=DEV, k_rho=0.9)
+    cache = synth.build_cache(k, v)
+    a = run_queue(q, k, v, cache, flags=ca.FLAG_BLOCK128)
+    b = run_queue(q, k, v, cache, flags=ca.FLAG_BLOCK256)
+    assert torch.equal(a, b)
 
 
 # -------------------------------------------------------------------- full attention
 
+@pytest.mark.parametrize("flags", FLAGS)
 @pytest.mark.parametrize("B,lq,lkv,H,D,shared", [(1, 300, 300, 2, 128, False),
                                                  (3, 200, 77, 2, 128, True),
                                                  (2, 129, 1, 1, 64, False),
                                                  (4, 64, 512, 3, 128, True)])
-def test_full_small_parity(B, lq, lkv, H, D, shared):
-    say("case full", B, lq, lkv, H, D, shared)
+def test_full_small_parity(B, lq, lkv, H, D, shared, flags):
+    say("case full", B, lq, lkv, H, D, shared, flags)
     q = synth.normal((B, lq, H, D), 12, 1, DEV)
     kb = 1 if shared else B
     k = synth.normal((kb, lkv, H, D), 12, 2, DEV)
     v = synth.normal((kb, lkv, H, D), 12, 3, DEV)
-    out = ca.full(q, k, v)
+    out = ca.full(q, k, v, ctx=ca.create(0, flags))
     torch.cuda.synchronize()
     ref = oracle.full(q, k, v)
     assert_parity(to_f64(out), ref, "full small")

@@ -122,12 +122,12 @@ def _slot_to_work_reference(n, n_xcd):
     return order
 
 
+@pytest.mark.parametrize("bm", [128, 256])
 @pytest.mark.parametrize("L,n,H,xcd", [(128, 4, 2, 8), (6240, 8, 12, 8), (97, 5, 3, 8),
                                        (1, 1, 1, 8), (300, 3, 7, 1), (6240, 8, 40, 8),
                                        (14400, 16, 40, 8), (200, 2, 3, 3)])
-def test_plan_matches_oracle_index_map(L, n, H, xcd):
-    items = ca.plan_debug(L, n, H, xcd)
-    bm = ca.block_rows()
+def test_plan_matches_oracle_index_map(L, n, H, xcd, bm):
+    items = ca.plan_debug(L, n, H, xcd, bm)
     nq = -(-L // bm)
     assert items.shape == (n * H * nq, 7)
     # every (chunk, head, query row) exactly once
@@ -149,6 +149,16 @@ def test_plan_matches_oracle_index_map(L, n, H, xcd):
         np.testing.assert_array_equal(plan_src, src)
         np.testing.assert_array_equal(plan_ch, ch)
         np.testing.assert_array_equal(plan_row, row)
+
+
+def test_default_block_rows():
+    assert ca.block_rows() in (128, 256)
+    np.testing.assert_array_equal(ca.plan_debug(300, 3, 2, 8),
+                                  ca.plan_debug(300, 3, 2, 8, ca.block_rows()))
+    assert ca.plan_debug(300, 3, 2, 8, 128).shape[0] == 3 * 2 * 3
+    assert ca.plan_debug(300, 3, 2, 8, 256).shape[0] == 3 * 2 * 2
+    with pytest.raises(ca.ChunkAttnError):
+        ca.plan_debug(300, 3, 2, 8, 96)
 
 
 def test_plan_order_longest_first_and_die_ranges():

@@ -176,7 +176,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;  // lane half
@@ -214,16 +214,14 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
   // ---- per-lane load map: LDS chunk c = wave*kCpw + i receives, at byte
   // c*1024 + lane*16, tile row r = c*kRowsPerKB + lane/kBlk and physical block
   // lane%kBlk, i.e. logical block (lane%kBlk) ^ swizzle(r).
-  int lrow[kCpw];
-  uint32_t koffs[kCpw], voffs[kCpw];  // element offsets within a one-segment tile
+  auto lrow = [&](int i) { return (wave * kCpw + i) * G::kRowsPerKB + lane / G::kBlk; };
+  uint32_t koffs[kCpw], voffs[kCpw];  // byte offsets within a one-segment tile
 #pragma unroll
   for (int i = 0; i < kCpw; ++i) {
-    const int c = wave * kCpw + i;
-    const int r = c * G::kRowsPerKB + lane / G::kBlk;
+    const int r = lrow(i);
     const int pb = lane % G::kBlk;
-    lrow[i] = r;
-    koffs[i] = (uint32_t)(r * rs + ((pb ^ k_swz<D>(r)) * 8));
-    voffs[i] = (uint32_t)(r * rs + ((pb ^ v_swz<D>(r)) * 8));
+    koffs[i] = (uint32_t)((r * rs + ((pb ^ k_swz<D>(r)) * 8)) * sizeof(T));
+    voffs[i] = (uint32_t)((r * rs + ((pb ^ v_swz<D>(r)) * 8)) * sizeof(T));
   }
 
   // Issues the loads of tile t into LDS buffer `buf`.
@@ -236,8 +234,8 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
         // whole tile in one segment: uniform base + fixed per-lane offsets
         const bool in_pred = r0 + kBN <= pred;
         const int64_t row = in_pred ? r0 : r0 - pred;
-        const T* kbase = (in_pred ? kpre : kown) + row * rs;
-        const T* vbase = (in_pred ? vpre : vown) + row * rs;
+        const char* kbase = reinterpret_cast<const char*>((in_pred ? kpre : kown) + row * rs);
+        const char* vbase = reinterpret_cast<const char*>((in_pred ? vpre : vown) + row * rs);
 #pragma unroll
         for (int i = 0; i < kCpw; ++i) {
           const int c = wave * kCpw + i;
@@ -250,11 +248,12 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
 #pragma unroll
         for (int i = 0; i < kCpw; ++i) {
           const int c = wave * kCpw + i;
-          int j = r0 + lrow[i];
+          const int r = lrow(i);
+          int j = r0 + r;
           j = j < total ? j : total - 1;
           const int pb = lane % G::kBlk;
-          const int kblk = pb ^ k_swz<D>(lrow[i]);
-          const int vblk = pb ^ v_swz<D>(lrow[i]);
+          const int kblk = pb ^ k_swz<D>(r);
+          const int vblk = pb ^ v_swz<D>(r);
           const T* kr = j < pred ? kpre + j * rs : kown + (j - pred) * rs;
           const T* vr = j < pred ? vpre + j * rs : vown + (j - pred) * rs;
           load_lds16(kr + kblk * 8, kb + c * 1024);
@@ -266,13 +265,14 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
 #pragma unroll
       for (int i = 0; i < kCpw; ++i) {
         const int c = wave * kCpw + i;
-        int j = r0 + lrow[i];
+        const int r = lrow(i);
+        int j = r0 + r;
         j = j < total ? j : total - 1;
         const int pb = lane % G::kBlk;
         const T* kr = j < pred ? kpre + j * rs : kown + (j - pred) * rs;
         const T* vr = j < pred ? vpre + j * rs : vown + (j - pred) * rs;
-        const u32x4_t kv = Io<T>::load8(kr + (pb ^ k_swz<D>(lrow[i])) * 8);
-        const u32x4_t vv = Io<T>::load8(vr + (pb ^ v_swz<D>(lrow[i])) * 8);
+        const u32x4_t kv = Io<T>::load8(kr + (pb ^ k_swz<D>(r)) * 8);
+        const u32x4_t vv = Io<T>::load8(vr + (pb ^ v_swz<D>(r)) * 8);
         *reinterpret_cast<u32x4_t*>(kb + c * 1024 + lane * 16) = kv;
         *reinterpret_cast<u32x4_t*>(vb + c * 1024 + lane * 16) = vv;
       }
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = -__builtin_inff();  // running max, log2 domain (score * scale * log2 e)
-  float l_run = 0.f;                // this lane half's share of the softmax denominator
+  float l4[4] = {0.f, 0.f, 0.f, 0.f};  // this lane half's share of the denominator
   const float s2 = a.scale_log2;
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -355,20 +355,30 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
         }
     }
 
-    // tile max of this lane's query row, then across the two lane halves
-    float mx = sacc[0][0];
+    // tile max over this lane's 32 scores (a balanced tree).  The two lane
+    // halves hold the other 32 keys of the same rows; they only need to agree
+    // on m, which changes rarely: each lane tests its own half against the
+    // running max, and only when some lane exceeds it by 2^8 do the halves
+    // exchange their maxima and raise m together.
+    float mx;
+    {
+      float t8[8];
 #pragma unroll
-    for (int kb2 = 0; kb2 < kBN / 32; ++kb2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb2][i]);
-    mx = fmaxf(mx, other_half(mx));
-    const float mxs = mx * s2;
-    if (__builtin_amdgcn_ballot_w64(mxs > m_run + kRescaleLog2) != 0) {
-      const float m_new = fmaxf(m_run, mxs);
+      for (int i = 0; i < 8; ++i) {
+        const int kb2 = i >> 2, j = (i & 3) * 4;
+        t8[i] = fmaxf(fmaxf(sacc[kb2][j], sacc[kb2][j + 1]),
+                      fmaxf(sacc[kb2][j + 2], sacc[kb2][j + 3]));
+      }
+      mx = fmaxf(fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3])),
+                 fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7])));
+    }
+    if (__builtin_amdgcn_ballot_w64(mx * s2 > m_run + kRescaleLog2) != 0) {
+      const float m_new = fmaxf(m_run, fmaxf(mx, other_half(mx)) * s2);
       const float alpha =
           m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
-      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l4[i] *= alpha;
 #pragma unroll
       for (int db = 0; db < kDb; ++db)
 #pragma unroll
@@ -388,8 +398,9 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
           if (key0 + 1 >= total) p1 = 0.f;
         }
         pk[kb2][i] = pack_bf16(p0, p1);
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[kb2][i]), ones,
-                                                l_run, false);
+        const int acc = (kb2 * 8 + i) & 3;  // four independent partial sums
+        l4[acc] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[kb2][i]), ones,
+                                                  l4[acc], false);
       }
     }
 
@@ -451,7 +462,8 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
   }
 
   // ---- epilogue: normalise and store this lane's query row
-  const float l_tot = l_run + other_half(l_run);
+  const float l_half = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+  const float l_tot = l_half + other_half(l_half);
   const float inv = 1.0f / l_tot;
   if (qvalid) {
     T* ob = static_cast<T*>(a.o) + it.b * a.q_bstride + (int64_t)qrow * rs + (int64_t)it.h * D;

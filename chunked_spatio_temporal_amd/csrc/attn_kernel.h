@@ -12,12 +12,20 @@
 //   S^T = K . Q^T      keys on the M side, queries on N: each lane ends up
 //                      holding 32 scores of ONE query row (its column), so the
 //                      softmax statistics of a row live in one lane pair.
-//   online softmax     running max m and sum l per query row in the log2
-//                      domain (scale*log2(e) folded into one FMA before exp2);
-//                      m is only raised when a tile's maximum exceeds it by
-//                      more than 2^8, which is exact (O and l share m) and
-//                      skips almost every rescale of O.  P is rounded to bf16
-//                      once and l is summed from the rounded P.
+//   softmax            sum l per query row in the log2 domain (scale*log2(e)
+//                      folded into one FMA before exp2), with a reference
+//                      maximum m shared by O and l, so any m gives the exact
+//                      result as long as nothing overflows.  Two schedules:
+//                      fixed m   m is the row maximum of the first tile and
+//                                never changes (no max, rescale or branch per
+//                                tile); a work item whose l or O comes out
+//                                non-finite marks its output and is redone by
+//                                chunk_attn_recheck with the running m.
+//                      running m m is raised only when a tile's maximum
+//                                exceeds it by more than 2^8, skipping almost
+//                                every rescale of O.
+//                      P is rounded to bf16 once and l is summed from the
+//                      rounded P.
 //   O^T += V^T . P^T   P^T comes straight out of the S^T accumulators as the
 //                      B operand; V^T is read from row-major V in LDS with the
 //                      transposing LDS read (ds_read_b64_tr_b16).  O^T again
@@ -37,6 +45,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "plan.h"
 
@@ -157,6 +167,18 @@ __device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32);
 // write LDS directly) has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup barrier that leaves in-flight global->LDS loads alone (unlike
+// __syncthreads, whose release fence waits for every outstanding global load).
+// LDS operations of this wave complete first (lgkmcnt(0)); loads whose data the
+// barrier must publish are waited for explicitly with wait_vmem().  The signal
+// fences keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 struct NoMask {
   static constexpr bool value = false;
 };
@@ -168,12 +190,24 @@ struct Mask {
   static constexpr bool value = true;
 };
 
-template <int D, typename T, int W>
-__global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
+// Marks a work item whose fixed-maximum pass overflowed: a quiet NaN in the
+// first element of its first query row (the output of finite inputs is finite).
+template <typename T>
+__device__ __forceinline__ T overflow_marker() {
+  return __builtin_bit_cast(T, std::conditional_t<sizeof(T) == 2, uint16_t, uint32_t>(
+                                   sizeof(T) == 2 ? 0x7FC0u : 0x7FC00000u));
+}
+
+// One work item with the synchronous schedule: every wave of the workgroup
+// computes S, the softmax and P.V of the same tile, one barrier per tile.
+// kFixed selects the fixed-maximum softmax (see the file header); without it
+// the running maximum is used and the result is always final.
+template <int D, typename T, int W, bool kFixed>
+__device__ __forceinline__ void attn_item_sync(const KernelArgs& a, const Item& it,
+                                               unsigned char* smem) {
   using G = Geo<D>;
   constexpr int kCpw = G::kChunks / W;  // 1 KB load chunks per wave per matrix
   static_assert(kCpw * W == G::kChunks, "tile split across waves");
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -181,8 +215,6 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;  // lane half
 
-  const int64_t w = slot_to_work(blockIdx.x, a.plan.n_items, a.plan.n_xcd);
-  const Item it = decode(a.plan, w);
   const int pred = it.pred_rows;
   const int total = pred + it.own_rows;
   const int n_tiles = (total + kBN - 1) / kBN;
@@ -214,7 +246,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
   // ---- per-lane load map: LDS chunk c = wave*kCpw + i receives, at byte
   // c*1024 + lane*16, tile row r = c*kRowsPerKB + lane/kBlk and physical block
   // lane%kBlk, i.e. logical block (lane%kBlk) ^ swizzle(r).
-  auto lrow = [&](int i) { return (wave * kCpw + i) * G::kRowsPerKB + lane / G::kBlk; };
+  auto lrow = [&](int i) __attribute__((always_inline)) { return (wave * kCpw + i) * G::kRowsPerKB + lane / G::kBlk; };
   uint32_t koffs[kCpw], voffs[kCpw];  // byte offsets within a one-segment tile
 #pragma unroll
   for (int i = 0; i < kCpw; ++i) {
@@ -225,7 +257,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
   }
 
   // Issues the loads of tile t into LDS buffer `buf`.
-  auto load_tile = [&](int t, int buf) {
+  auto load_tile = [&](int t, int buf) __attribute__((always_inline)) {
     unsigned char* kb = smem + buf * G::kBufBytes;
     unsigned char* vb = kb + G::kTileBytes;
     const int r0 = t * kBN;
@@ -323,7 +355,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
 
   // One tile: S^T, online softmax, O^T update.  kBuf: LDS buffer (compile-time
   // so that it folds into the immediate offsets).  Mask: keys >= total are out.
-  auto compute = [&](int t, auto buf_tag, auto mask_tag) {
+  auto compute = [&](int t, auto buf_tag, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
     constexpr uint32_t kKBase = decltype(buf_tag)::value * G::kBufBytes;
     constexpr uint32_t kVBase = kKBase + G::kTileBytes;
@@ -356,12 +388,9 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
     }
 
     // tile max over this lane's 32 scores (a balanced tree).  The two lane
-    // halves hold the other 32 keys of the same rows; they only need to agree
-    // on m, which changes rarely: each lane tests its own half against the
-    // running max, and only when some lane exceeds it by 2^8 do the halves
-    // exchange their maxima and raise m together.
-    float mx;
-    {
+    // halves hold the other 32 keys of the same rows and exchange their maxima
+    // whenever m is set.
+    auto tile_max = [&]() __attribute__((always_inline)) {
       float t8[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -369,20 +398,32 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
         t8[i] = fmaxf(fmaxf(sacc[kb2][j], sacc[kb2][j + 1]),
                       fmaxf(sacc[kb2][j + 2], sacc[kb2][j + 3]));
       }
-      mx = fmaxf(fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3])),
-                 fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7])));
-    }
-    if (__builtin_amdgcn_ballot_w64(mx * s2 > m_run + kRescaleLog2) != 0) {
-      const float m_new = fmaxf(m_run, fmaxf(mx, other_half(mx)) * s2);
-      const float alpha =
-          m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+      return fmaxf(fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3])),
+                   fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7])));
+    };
+    if constexpr (kFixed) {
+      // m from the first tile (which always holds valid keys); O and l are
+      // still zero there, so nothing is rescaled.
+      if (t == 0) {
+        const float mx = tile_max();
+        m_run = fmaxf(mx, other_half(mx)) * s2;
+      }
+    } else {
+      // each lane tests its own half against the running max; only when some
+      // lane exceeds it by 2^8 do the halves agree on a new m together
+      const float mx = tile_max();
+      if (__builtin_amdgcn_ballot_w64(mx * s2 > m_run + kRescaleLog2) != 0) {
+        const float m_new = fmaxf(m_run, fmaxf(mx, other_half(mx)) * s2);
+        const float alpha =
+            m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) l4[i] *= alpha;
+        for (int i = 0; i < 4; ++i) l4[i] *= alpha;
 #pragma unroll
-      for (int db = 0; db < kDb; ++db)
+        for (int db = 0; db < kDb; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      }
     }
 
     uint32_t pk[kBN / 32][8];
@@ -431,7 +472,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
 
   // One pipeline step: start loading tile t+1 into the other buffer, compute
   // tile t, then wait for the loads and synchronise the workgroup.
-  auto step = [&](int t, auto buf_tag, auto mask_tag) {
+  auto step = [&](int t, auto buf_tag, auto mask_tag) __attribute__((always_inline)) {
     constexpr int kB = decltype(buf_tag)::value;
     if (t + 1 < n_tiles) load_tile(t + 1, kB ^ 1);
     compute(t, buf_tag, mask_tag);
@@ -461,8 +502,22 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
       step(t, Buf<0>{}, Mask{});
   }
 
-  // ---- epilogue: normalise and store this lane's query row
+  // ---- epilogue: (fixed m) overflow check over the workgroup, then
+  // normalise and store this lane's query row
   const float l_half = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+  if constexpr (kFixed) {
+    float acc = l_half;
+#pragma unroll
+    for (int db = 0; db < kDb; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc += oacc[db][i];
+    if (__syncthreads_or(!__builtin_isfinite(acc))) {
+      if (tid == 0)
+        static_cast<T*>(a.o)[it.b * a.q_bstride + (int64_t)it.q0 * rs + (int64_t)it.h * D] =
+            overflow_marker<T>();
+      return;
+    }
+  }
   const float l_tot = l_half + other_half(l_half);
   const float inv = 1.0f / l_tot;
   if (qvalid) {
@@ -476,6 +531,27 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
                       oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
       }
   }
+}
+
+// Main pass: one work item per workgroup, fixed-maximum softmax.
+template <int D, typename T, int W>
+__global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const Item it = decode(a.plan, slot_to_work(blockIdx.x, a.plan.n_items, a.plan.n_xcd));
+  attn_item_sync<D, T, W, true>(a, it, smem);
+}
+
+// Second pass, launched after chunk_attn_fwd on the same stream with the same
+// grid: recomputes with the running maximum every work item whose first output
+// element carries the overflow marker; the others return after one load.
+template <int D, typename T, int W>
+__global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_recheck(KernelArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const Item it = decode(a.plan, slot_to_work(blockIdx.x, a.plan.n_items, a.plan.n_xcd));
+  const T first = static_cast<const T*>(a.o)[it.b * a.q_bstride + (int64_t)it.q0 * a.row_stride +
+                                              (int64_t)it.h * D];
+  if (!__builtin_isnan((float)first)) return;
+  attn_item_sync<D, T, W, false>(a, it, smem);
 }
 
 // Writes the decoded work item of every workgroup slot (7 ints each), using

@@ -142,22 +142,36 @@ int validate_full(std::string* err, const void* q, const void* k, const void* v,
 // Every kernel configuration the host can launch, instantiated explicitly.
 namespace chunkattn {
 template __global__ void chunk_attn_fwd<128, __bf16, 4>(KernelArgs);
-template __global__ void chunk_attn_fwd<128, __bf16, 8>(KernelArgs);
+template __global__ void chunk_attn_recheck<128, __bf16, 4>(KernelArgs);
 template __global__ void chunk_attn_fwd<128, float, 4>(KernelArgs);
-template __global__ void chunk_attn_fwd<128, float, 8>(KernelArgs);
+template __global__ void chunk_attn_recheck<128, float, 4>(KernelArgs);
 template __global__ void chunk_attn_fwd<64, __bf16, 4>(KernelArgs);
-template __global__ void chunk_attn_fwd<64, __bf16, 8>(KernelArgs);
+template __global__ void chunk_attn_recheck<64, __bf16, 4>(KernelArgs);
 template __global__ void chunk_attn_fwd<64, float, 4>(KernelArgs);
+template __global__ void chunk_attn_recheck<64, float, 4>(KernelArgs);
+template __global__ void chunk_attn_fwd<128, __bf16, 8>(KernelArgs);
+template __global__ void chunk_attn_recheck<128, __bf16, 8>(KernelArgs);
+template __global__ void chunk_attn_fwd<128, float, 8>(KernelArgs);
+template __global__ void chunk_attn_recheck<128, float, 8>(KernelArgs);
+template __global__ void chunk_attn_fwd<64, __bf16, 8>(KernelArgs);
+template __global__ void chunk_attn_recheck<64, __bf16, 8>(KernelArgs);
 template __global__ void chunk_attn_fwd<64, float, 8>(KernelArgs);
+template __global__ void chunk_attn_recheck<64, float, 8>(KernelArgs);
 }  // namespace chunkattn
 
 namespace {
 
+// W waves x 32 query rows per work item, synchronous schedule: the
+// fixed-maximum pass, then the overflow recheck on the same stream.
 template <int D, typename T, int W>
 hipError_t launch_t(const KernelArgs& a, hipStream_t stream) {
   using G = chunkattn::Geo<D>;
   const dim3 grid((unsigned)a.plan.n_items);
-  hipLaunchKernelGGL((chunkattn::chunk_attn_fwd<D, T, W>), grid, dim3(W * 64),
+  hipLaunchKernelGGL((chunkattn::chunk_attn_fwd<D, T, W>), grid, dim3(64 * W), 2 * G::kBufBytes,
+                     stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((chunkattn::chunk_attn_recheck<D, T, W>), grid, dim3(64 * W),
                      2 * G::kBufBytes, stream, a);
   return hipGetLastError();
 }

@@ -333,3 +333,23 @@ def test_full_sequence_workload_sampled_parity():
     ref = oracle.full_rows(q.cpu(), k.cpu(), v.cpu(), rows, w.scale)
     s = assert_parity(gather_rows(out, rows), ref, "full32k")
     say("full32k sampled rows", len(rows), s)
+
+
+@pytest.mark.parametrize("flags", FLAGS)
+def test_score_overflow_falls_back_exactly(flags):
+    """Scores that rise far above a row's first tile (2^300 in the exponent)
+    overflow a fixed-maximum softmax; the kernel must still return the exact
+    softmax (here all weight on the high-scoring keys), via its running-max
+    fallback.  Chunk 1's own rows carry the high keys, chunk 0's do not."""
+    n, L, H, D = 2, 200, 2, 128
+    q = torch.full((n, L, H, D), 20.0, dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros((n, L, H, D), dtype=torch.bfloat16, device=DEV)
+    k[1, 150:] = 1.0            # logical rows 350.. of chunk 1: score 20*128/sqrt(128) = 226
+    v = synth.normal((n, L, H, D), 15, 3, DEV)
+    cache = synth.build_cache(k, v)
+    out = run_queue(q, k, v, cache, flags=flags)
+    ref = oracle.queue_step(q, k, v, cache)
+    assert_parity(to_f64(out), ref, "overflow fallback")
+    # chunk 1 averages V over its 50 high-scoring own rows
+    exp1 = v[1, 150:].float().mean(0)
+    torch.testing.assert_close(out[1].float(), exp1.expand(L, H, D), atol=1e-2, rtol=0)

@@ -198,10 +198,14 @@ __device__ __forceinline__ T overflow_marker() {
                                    sizeof(T) == 2 ? 0x7FC0u : 0x7FC00000u));
 }
 
+// LDS bytes of the synchronous schedule: two K/V tile buffers.
+template <int D>
+constexpr uint32_t kSyncLdsBytes = 2 * Geo<D>::kBufBytes;
+
 // One work item with the synchronous schedule: every wave of the workgroup
 // computes S, the softmax and P.V of the same tile, one barrier per tile.
-// kFixed selects the fixed-maximum softmax (see the file header); without it
-// the running maximum is used and the result is always final.
+// K/V tiles are double buffered in LDS.  kFixed selects the fixed-maximum softmax (see the file header);
+// without it the running maximum is used and the result is always final.
 template <int D, typename T, int W, bool kFixed>
 __device__ __forceinline__ void attn_item_sync(const KernelArgs& a, const Item& it,
                                                unsigned char* smem) {
@@ -257,8 +261,7 @@ __device__ __forceinline__ void attn_item_sync(const KernelArgs& a, const Item& 
   }
 
   // Issues the loads of tile t into LDS buffer `buf`.
-  auto load_tile = [&](int t, int buf) __attribute__((always_inline)) {
-    unsigned char* kb = smem + buf * G::kBufBytes;
+  auto load_tile = [&](int t, unsigned char* kb) __attribute__((always_inline)) {
     unsigned char* vb = kb + G::kTileBytes;
     const int r0 = t * kBN;
     if constexpr (sizeof(T) == 2) {
@@ -351,14 +354,14 @@ __device__ __forceinline__ void attn_item_sync(const KernelArgs& a, const Item& 
         voff_lds[db][w2] = v_off<D>(r, col >> 3) + ((col >> 2) & 1) * 8;
       }
   }
-  CA_LDS unsigned char* lds = (CA_LDS unsigned char*)smem;
 
   // One tile: S^T, online softmax, O^T update.  kBuf: LDS buffer (compile-time
   // so that it folds into the immediate offsets).  Mask: keys >= total are out.
-  auto compute = [&](int t, auto buf_tag, auto mask_tag) __attribute__((always_inline)) {
+  auto compute = [&](int t, const unsigned char* buf, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
-    constexpr uint32_t kKBase = decltype(buf_tag)::value * G::kBufBytes;
-    constexpr uint32_t kVBase = kKBase + G::kTileBytes;
+    constexpr uint32_t kKBase = 0;
+    constexpr uint32_t kVBase = G::kTileBytes;
+    const CA_LDS unsigned char* lds = (const CA_LDS unsigned char*)buf;
 
     f32x16_t sacc[kBN / 32];
 #pragma unroll
@@ -471,35 +474,41 @@ __device__ __forceinline__ void attn_item_sync(const KernelArgs& a, const Item& 
   };
 
   // One pipeline step: start loading tile t+1 into the other buffer, compute
-  // tile t, then wait for the loads and synchronise the workgroup.
-  auto step = [&](int t, auto buf_tag, auto mask_tag) __attribute__((always_inline)) {
-    constexpr int kB = decltype(buf_tag)::value;
-    if (t + 1 < n_tiles) load_tile(t + 1, kB ^ 1);
-    compute(t, buf_tag, mask_tag);
+  // tile t, then wait for the loads and synchronise the workgroup.  The two
+  // buffers are restrict pointers: the compiler then knows that the LDS reads
+  // of tile t do not touch the buffer being filled, and does not make them
+  // wait for those loads.
+  auto step = [&](int t, unsigned char* __restrict__ cur, unsigned char* __restrict__ nxt,
+                  auto mask_tag) __attribute__((always_inline)) {
+    if (t + 1 < n_tiles) load_tile(t + 1, nxt);
+    compute(t, cur, mask_tag);
     wait_vmem();
-    __syncthreads();
+    wg_barrier();
   };
+  unsigned char* const buf0 = smem;
+  unsigned char* const buf1 = smem + G::kBufBytes;
 
-  load_tile(0, 0);
+  load_tile(0, buf0);
   wait_vmem();
-  __syncthreads();
-  // full tiles in pairs (buffer 0, buffer 1), so the buffer is a constant
+  wg_barrier();
+  // full tiles in pairs (buffer 0, buffer 1), so every buffer address is a
+  // constant
   const int n_full = total / kBN;
   int t = 0;
   for (; t + 2 <= n_full; t += 2) {
-    step(t, Buf<0>{}, NoMask{});
-    step(t + 1, Buf<1>{}, NoMask{});
+    step(t, buf0, buf1, NoMask{});
+    step(t + 1, buf1, buf0, NoMask{});
   }
   if (t < n_full) {
-    step(t, Buf<0>{}, NoMask{});
+    step(t, buf0, buf1, NoMask{});
     ++t;
   }
   // the ragged last tile, if any
   if (t < n_tiles) {
     if (t & 1)
-      step(t, Buf<1>{}, Mask{});
+      step(t, buf1, buf0, Mask{});
     else
-      step(t, Buf<0>{}, Mask{});
+      step(t, buf0, buf1, Mask{});
   }
 
   // ---- epilogue: (fixed m) overflow check over the workgroup, then

@@ -165,14 +165,13 @@ namespace {
 // fixed-maximum pass, then the overflow recheck on the same stream.
 template <int D, typename T, int W>
 hipError_t launch_t(const KernelArgs& a, hipStream_t stream) {
-  using G = chunkattn::Geo<D>;
   const dim3 grid((unsigned)a.plan.n_items);
-  hipLaunchKernelGGL((chunkattn::chunk_attn_fwd<D, T, W>), grid, dim3(64 * W), 2 * G::kBufBytes,
-                     stream, a);
+  constexpr uint32_t kLds = chunkattn::kSyncLdsBytes<D>;
+  hipLaunchKernelGGL((chunkattn::chunk_attn_fwd<D, T, W>), grid, dim3(64 * W), kLds, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((chunkattn::chunk_attn_recheck<D, T, W>), grid, dim3(64 * W),
-                     2 * G::kBufBytes, stream, a);
+  hipLaunchKernelGGL((chunkattn::chunk_attn_recheck<D, T, W>), grid, dim3(64 * W), kLds, stream,
+                     a);
   return hipGetLastError();
 }
 

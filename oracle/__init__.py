@@ -16,6 +16,12 @@ Parity status of each entry point (what pins it, in tests/test_oracle_pins.py):
   queue_probs              pinned: rows sum to 1, closed-form weights
   full / full_rows         pinned: torch SDPA, n_chunks=1 reduction, closed forms
   index_map                pinned: brute-force enumeration of the band mask
+  window_step / window_rows
+                           pinned: brute-force masked attention over the
+                           concatenated sequence with the three-chunk window
+                           mask, single-chunk reduction to full attention,
+                           constant-V and closed forms, golden fixtures
+  window_index_map         pinned: brute-force enumeration of the window mask
 """
 import ctypes
 import os
@@ -54,6 +60,15 @@ def _load():
     lib.oracle_queue_probs.restype = i32
     lib.oracle_queue_probs.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i64, dbl,
                                        i64, i64, i64, vp, vp]
+    lib.oracle_window_q_rows.restype = i64
+    lib.oracle_window_q_rows.argtypes = [i64, i64, i64]
+    lib.oracle_window_kv_set_size.restype = i64
+    lib.oracle_window_kv_set_size.argtypes = [i64, i64, i64]
+    lib.oracle_window_index_map.restype = i64
+    lib.oracle_window_index_map.argtypes = [i64, i64, i64, vp, vp, vp]
+    lib.oracle_window_rows.restype = i32
+    lib.oracle_window_rows.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i64, dbl, vp, i64,
+                                       vp]
     lib.oracle_full_rows.restype = i32
     lib.oracle_full_rows.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl,
                                      vp, i64, vp]
@@ -209,4 +224,51 @@ def full_rows(q, k, v, rows, scale=None) -> np.ndarray:
                                   H, D, scale, _ptr(rows), rows.shape[0], _ptr(out))
     if rc != 0:
         raise RuntimeError(f"oracle_full_rows failed ({rc})")
+    return out
+
+
+def window_q_rows(chunk_len: int, n_chunks: int, c: int) -> int:
+    return int(_load().oracle_window_q_rows(chunk_len, n_chunks, c))
+
+
+def window_kv_set_size(chunk_len: int, n_chunks: int, c: int) -> int:
+    return int(_load().oracle_window_kv_set_size(chunk_len, n_chunks, c))
+
+
+def window_index_map(chunk_len: int, n_chunks: int, c: int):
+    """(src, chunk, row) int64 arrays describing W_c entry by entry."""
+    lib = _load()
+    m = window_kv_set_size(chunk_len, n_chunks, c)
+    src = np.empty(m, np.int64)
+    ch = np.empty(m, np.int64)
+    row = np.empty(m, np.int64)
+    got = lib.oracle_window_index_map(chunk_len, n_chunks, c, _ptr(src), _ptr(ch), _ptr(row))
+    if got != m:
+        raise ValueError("oracle_window_index_map: bad arguments")
+    return src, ch, row
+
+
+def window_step(q, k, v, kv_cache=None, scale=None) -> np.ndarray:
+    """Whole window step; returns fp64 [n_chunks][2][L][H][D] (window c: chunk c's
+    query rows, then chunk c+1's; the second half of the last window is NaN)."""
+    qa, ka, va, ca, dt, (n, L, H, D) = _common(q, k, v, kv_cache)
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    out = np.empty((n, 2, L, H, D), np.float64)
+    rc = _load().oracle_window_rows(dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(ca), L, n, H, D,
+                                    scale, None, 0, _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"oracle_window_rows failed ({rc})")
+    return out
+
+
+def window_rows(q, k, v, kv_cache, rows, scale=None) -> np.ndarray:
+    """Selected window-step rows; rows is (N, 3) of (window, head, row in [0, 2L))."""
+    qa, ka, va, ca, dt, (n, L, H, D) = _common(q, k, v, kv_cache)
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    rows = np.ascontiguousarray(np.asarray(rows, np.int64).reshape(-1, 3))
+    out = np.empty((rows.shape[0], D), np.float64)
+    rc = _load().oracle_window_rows(dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(ca), L, n, H, D,
+                                    scale, _ptr(rows), rows.shape[0], _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"oracle_window_rows failed ({rc})")
     return out

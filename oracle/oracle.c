@@ -32,6 +32,21 @@
  * cache buffer (slot c holds chunk c-1's K then V) or, when no cache buffer is
  * given, straight from chunk c-1's own K/V.
  *
+ * Window step (same page, section 三, the form the cache is introduced for).
+ * Processing a window of three neighbouring chunks [B_{i-1}, B_i, B_{i+1}]
+ * would repeat B_{i+1}, which the window processed just before already
+ * handled; its self-attention K/V is cached there and reused, so the window's
+ * own input shrinks to [B_{i-1}, B_i].  Reading used here, with chunks indexed
+ * in processing order as above: window c is centred on chunk c (B_i); its
+ * queries are the rows of chunk c and of chunk c+1 (B_{i-1}, the next chunk
+ * to be processed), 2L rows, or L rows for the last window, which has no chunk
+ * c+1; its key/value set is
+ *     W_c = [predecessor rows (chunk c-1, if c >= 1)] ++ [own rows of chunk c]
+ *           ++ [own rows of chunk c+1 (if c+1 < n)]
+ * and each query row gets plain softmax attention over W_c, as above.  The
+ * output of window c holds its 2L query rows: out[c][0] = chunk c's rows,
+ * out[c][1] = chunk c+1's rows (absent for the last window).
+ *
  * Precision.  Every input element is widened exactly to fp64 (bf16 and fp32
  * both embed exactly); scores, exponentials, sums and the weighted sum are
  * fp64, the dot product summed in increasing dimension order.  Two passes per
@@ -41,6 +56,7 @@
  * Layouts (row-major, element offsets):
  *   q, k, v, out      [n_chunks][L][H][D]
  *   kv_cache          [n_chunks][2][L][H][D]   (slot c: K of c-1, then V of c-1)
+ *   window out        [n_chunks][2][L][H][D]   (window c: chunk c, then chunk c+1)
  *   full attention    q/out [batch][Lq][H][D],  k/v batch b at b*kv_batch_stride,
  *                     each [Lkv][H][D]
  */
@@ -148,11 +164,24 @@ typedef struct {
     /* full attention */
     int64_t kv_base;
     int full;
+    /* window step: W_c as listed by its index map */
+    const int64_t *map_src, *map_chunk, *map_row;
+    int window;
 } kv_source;
+
+static void window_entry(const void *k, const void *v, const void *kv_cache, int64_t L,
+                         int64_t H, int64_t D, int64_t c, int64_t h, int64_t src,
+                         int64_t chunk, int64_t row, const void **kb, int64_t *ko,
+                         const void **vb, int64_t *vo);
 
 static void row_kv(const kv_source *src, int64_t j, const void **kb, int64_t *ko,
                    const void **vb, int64_t *vo)
 {
+    if (src->window) {
+        window_entry(src->k, src->v, src->ck, src->L, src->H, src->D, src->c, src->h,
+                     src->map_src[j], src->map_chunk[j], src->map_row[j], kb, ko, vb, vo);
+        return;
+    }
     if (src->full) {
         *kb = src->k;
         *vb = src->v;
@@ -374,6 +403,151 @@ int oracle_full_rows(int dtype, const void *q, const void *k, const void *v,
             }
             free(s);
         }
+    }
+    return bad ? -2 : 0;
+}
+
+/* ---- window step ------------------------------------------------------- */
+
+/* Query rows of window c: chunk c, and chunk c+1 when it exists. */
+int64_t oracle_window_q_rows(int64_t chunk_len, int64_t n_chunks, int64_t c)
+{
+    return c + 1 < n_chunks ? 2 * chunk_len : chunk_len;
+}
+
+/* Size of W_c. */
+int64_t oracle_window_kv_set_size(int64_t chunk_len, int64_t n_chunks, int64_t c)
+{
+    int64_t m = chunk_len;                 /* own rows of chunk c */
+    if (c >= 1)
+        m += chunk_len;                    /* cached rows of chunk c-1 */
+    if (c + 1 < n_chunks)
+        m += chunk_len;                    /* own rows of chunk c+1 */
+    return m;
+}
+
+/* W_c entry by entry: (source, chunk, token row), in the order stated above. */
+int64_t oracle_window_index_map(int64_t chunk_len, int64_t n_chunks, int64_t c,
+                                int64_t *src, int64_t *chunk, int64_t *row)
+{
+    if (c < 0 || c >= n_chunks || chunk_len < 0)
+        return -1;
+    int64_t j = 0;
+    if (c >= 1)
+        for (int64_t r = 0; r < chunk_len; ++r, ++j) {
+            src[j] = ORACLE_SRC_PRED;
+            chunk[j] = c - 1;
+            row[j] = r;
+        }
+    for (int64_t r = 0; r < chunk_len; ++r, ++j) {
+        src[j] = ORACLE_SRC_OWN;
+        chunk[j] = c;
+        row[j] = r;
+    }
+    if (c + 1 < n_chunks)
+        for (int64_t r = 0; r < chunk_len; ++r, ++j) {
+            src[j] = ORACLE_SRC_OWN;
+            chunk[j] = c + 1;
+            row[j] = r;
+        }
+    return j;
+}
+
+/*
+ * Element offsets (head h, dim 0) of W_c entry j: a predecessor entry comes
+ * from cache slot c when a cache buffer is given (K half, then V half), else
+ * from chunk c-1's own K/V; an own entry from its chunk's K/V.
+ */
+static void window_entry(const void *k, const void *v, const void *kv_cache, int64_t L,
+                         int64_t H, int64_t D, int64_t c, int64_t h, int64_t src,
+                         int64_t chunk, int64_t row, const void **kb, int64_t *ko,
+                         const void **vb, int64_t *vo)
+{
+    if (src == ORACLE_SRC_PRED && kv_cache) {
+        *kb = kv_cache;
+        *vb = kv_cache;
+        *ko = (((c * 2 + 0) * L + row) * H + h) * D;
+        *vo = (((c * 2 + 1) * L + row) * H + h) * D;
+    } else {
+        *kb = k;
+        *vb = v;
+        *ko = ((chunk * L + row) * H + h) * D;
+        *vo = *ko;
+    }
+}
+
+/*
+ * Window step over selected rows: rows holds n_rows triples (window c, head h,
+ * row r) with r < oracle_window_q_rows(L, n, c); row r is chunk c's token r
+ * for r < L and chunk c+1's token r-L otherwise.  out: n_rows x D doubles.
+ * Pass rows = NULL for every row; out is then [n][2][L][H][D] with the absent
+ * half of the last window set to NaN.
+ */
+int oracle_window_rows(int dtype, const void *q, const void *k, const void *v,
+                       const void *kv_cache, int64_t L, int64_t n, int64_t H, int64_t D,
+                       double scale, const int64_t *rows, int64_t n_rows, double *out)
+{
+    if (L <= 0 || n <= 0 || H <= 0 || D <= 0)
+        return -1;
+    const int all = rows == NULL;
+    if (!all)
+        for (int64_t i = 0; i < n_rows; ++i) {
+            int64_t c = rows[3 * i], h = rows[3 * i + 1], r = rows[3 * i + 2];
+            if (c < 0 || c >= n || h < 0 || h >= H || r < 0 ||
+                r >= oracle_window_q_rows(L, n, c))
+                return -1;
+        }
+    const int64_t total = all ? n * 2 * L * H : n_rows;
+    const int64_t max_nk = 3 * L;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * max_nk);
+        int64_t *map = (int64_t *)malloc(sizeof(int64_t) * 3 * max_nk);
+        if (!s || !map) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+            int64_t map_c = -1, nk = 0;
+#pragma omp for schedule(dynamic, 8)
+            for (int64_t i = 0; i < total; ++i) {
+                int64_t c, h, r;
+                double *dst;
+                if (all) {
+                    /* out[c][half][row][h][:] */
+                    h = i % H;
+                    const int64_t rr = (i / H) % L, half = (i / (H * L)) % 2;
+                    c = i / (H * L * 2);
+                    r = half * L + rr;
+                    dst = out + i * D;
+                    if (r >= oracle_window_q_rows(L, n, c)) {
+                        for (int64_t d = 0; d < D; ++d)
+                            dst[d] = NAN;
+                        continue;
+                    }
+                } else {
+                    c = rows[3 * i];
+                    h = rows[3 * i + 1];
+                    r = rows[3 * i + 2];
+                    dst = out + i * D;
+                }
+                if (c != map_c) {
+                    nk = oracle_window_index_map(L, n, c, map, map + max_nk, map + 2 * max_nk);
+                    map_c = c;
+                }
+                const int64_t q_chunk = r < L ? c : c + 1;
+                const int64_t q_row = r < L ? r : r - L;
+                kv_source src = queue_source(k, v, kv_cache, c, h, L, H, D);
+                src.window = 1;
+                src.map_src = map;
+                src.map_chunk = map + max_nk;
+                src.map_row = map + 2 * max_nk;
+                attend_row(dtype, q, ((q_chunk * L + q_row) * H + h) * D, &src, nk, scale, s,
+                           dst, NULL);
+            }
+        }
+        free(s);
+        free(map);
     }
     return bad ? -2 : 0;
 }

@@ -32,6 +32,16 @@ MUTANTS = {
     "cache_ignored": ("*from_cache = 1;", "*from_cache = 0; *k_off = ((c - 1) * L + j) * H * D; *v_off = *k_off;"),
     "dot_truncated": ("for (int64_t d = 0; d < D; ++d)\n            acc +=",
                       "for (int64_t d = 0; d + 1 < D; ++d)\n            acc +="),
+    # window step
+    "window_next_chunk_is_self": ("chunk[j] = c + 1;", "chunk[j] = c;"),
+    "window_query_row_shift": ("const int64_t q_row = r < L ? r : r - L;",
+                               "const int64_t q_row = r < L ? r : (r - L + 1) % L;"),
+    "window_cache_slot_off_by_one": ("*ko = (((c * 2 + 0) * L + row) * H + h) * D;",
+                                     "*ko = ((((c - 1) * 2 + 0) * L + row) * H + h) * D;"),
+    "window_heads_mixed": ("*ko = ((chunk * L + row) * H + h) * D;",
+                           "*ko = ((chunk * L + row) * H + 0) * D;"),
+    "window_predecessor_dropped": ("if (c >= 1)\n        for (int64_t r = 0; r < chunk_len; ++r, ++j) {",
+                                   "if (0)\n        for (int64_t r = 0; r < chunk_len; ++r, ++j) {"),
 }
 
 

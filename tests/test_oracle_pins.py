@@ -337,3 +337,147 @@ def test_cache_slot0_is_never_read():
     assert np.isnan(cache[0]).all()
     got = oracle.queue_step(q, k, v, cache)
     assert np.isfinite(got).all()
+
+
+# --------------------------------------------------------------------------
+# window step (DualParal write-up, section 三: the window [B_{i-1}, B_i] with
+# the cached K/V of B_{i+1}; chunk c+1 plays B_{i-1}, chunk c-1 B_{i+1})
+
+WGOLDEN = os.path.join(os.path.dirname(__file__), "golden", "window_closed_forms.json")
+
+
+def _window_golden_cases():
+    with open(WGOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _window_golden_cases(), ids=lambda c: c["name"])
+def test_window_golden_closed_forms(case):
+    q = np.array(case["q"], np.float64)
+    k = np.array(case["k"], np.float64)
+    v = np.array(case["v"], np.float64)
+    cache = None if case["cache"] is None else np.array(case["cache"], np.float64)
+    got = oracle.window_step(q, k, v, cache, scale=case["scale"])
+    flat = [np.nan if x is None else x for x in np.array(case["expected"], dtype=object).ravel()]
+    exp = np.array(flat, np.float64).reshape(got.shape)
+    np.testing.assert_allclose(got, exp, rtol=0, atol=1e-12)
+
+
+def window_masked_attention(q, k, v, scale):
+    """Brute force over the concatenated sequence: window c's queries are the
+    tokens of chunks c and c+1, and each sees every key of chunks c-1, c, c+1
+    that exists.  Written independently of the oracle (dense scores per head).
+    Returns [n][2][L][H][D] with NaN for the absent half of the last window."""
+    n, L, H, D = q.shape
+    S = n * L
+    qs, ks, vs = q.reshape(S, H, D), k.reshape(S, H, D), v.reshape(S, H, D)
+    chunk_of = np.arange(S) // L
+    out = np.full((n, 2, L, H, D), np.nan)
+    for c in range(n):
+        qtok = np.flatnonzero((chunk_of == c) | (chunk_of == c + 1))
+        keys = np.flatnonzero((chunk_of >= c - 1) & (chunk_of <= c + 1))
+        for h in range(H):
+            s = scale * qs[qtok, h, :] @ ks[keys, h, :].T
+            s -= s.max(axis=1, keepdims=True)
+            w = np.exp(s)
+            w /= w.sum(axis=1, keepdims=True)
+            o = w @ vs[keys, h, :]
+            out[c].reshape(2 * L, H, D)[: len(qtok), h, :] = o
+    return out
+
+
+@pytest.mark.parametrize("shape", [(4, 6, 2, 8), (3, 5, 3, 4), (1, 7, 2, 3), (2, 1, 1, 2),
+                                   (5, 3, 2, 5)])
+@pytest.mark.parametrize("with_cache", [False, True])
+def test_window_equals_masked_concatenation(shape, with_cache):
+    q, k, v = rand(shape, 31), rand(shape, 32), rand(shape, 33)
+    cache = make_cache(k, v) if with_cache else None
+    got = oracle.window_step(q, k, v, cache, scale=0.7)
+    exp = window_masked_attention(q, k, v, 0.7)
+    np.testing.assert_allclose(got, exp, rtol=0, atol=1e-12)
+
+
+def test_window_equals_torch_sdpa_with_window_mask():
+    n, L, H, D = 4, 5, 2, 6
+    q, k, v = rand((n, L, H, D), 41), rand((n, L, H, D), 42), rand((n, L, H, D), 43)
+    got = oracle.window_step(q, k, v, None, scale=0.3)
+    S = n * L
+    chunk_of = torch.arange(S) // L
+    qt = torch.tensor(q.reshape(S, H, D)).permute(1, 0, 2)
+    kt = torch.tensor(k.reshape(S, H, D)).permute(1, 0, 2)
+    vt = torch.tensor(v.reshape(S, H, D)).permute(1, 0, 2)
+    for c in range(n):
+        sel = (chunk_of == c) | (chunk_of == c + 1)
+        mask = ((chunk_of[None, :] >= c - 1) & (chunk_of[None, :] <= c + 1)).expand(int(sel.sum()), S)
+        o = torch.nn.functional.scaled_dot_product_attention(qt[:, sel], kt, vt, attn_mask=mask,
+                                                              scale=0.3)
+        o = o.permute(1, 0, 2).numpy()
+        np.testing.assert_allclose(got[c].reshape(2 * L, H, D)[: o.shape[0]], o, rtol=0, atol=1e-12)
+
+
+def test_window_single_chunk_equals_full_and_queue():
+    L, H, D = 9, 2, 4
+    q, k, v = rand((1, L, H, D), 51), rand((1, L, H, D), 52), rand((1, L, H, D), 53)
+    got = oracle.window_step(q, k, v, None, scale=0.5)
+    assert np.isnan(got[0, 1]).all()
+    np.testing.assert_allclose(got[0, 0], oracle.full(q, k, v, scale=0.5)[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[0, 0], oracle.queue_step(q, k, v, None, scale=0.5)[0], rtol=0,
+                               atol=1e-12)
+
+
+def test_window_last_equals_queue_chunk():
+    """The last window (no next chunk) has exactly the queue step's key/value
+    set for that chunk: its predecessor and its own rows."""
+    n, L, H, D = 3, 4, 2, 5
+    q, k, v = rand((n, L, H, D), 61), rand((n, L, H, D), 62), rand((n, L, H, D), 63)
+    got = oracle.window_step(q, k, v, None, scale=0.8)
+    np.testing.assert_allclose(got[n - 1, 0], oracle.queue_step(q, k, v, None, scale=0.8)[n - 1],
+                               rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("with_cache", [False, True])
+def test_window_constant_v_returned(with_cache):
+    n, L, H, D = 3, 4, 2, 3
+    q, k = rand((n, L, H, D), 71), rand((n, L, H, D), 72)
+    v = np.broadcast_to(np.array([1.5, -2.0, 0.25]), (n, L, H, D)).copy()
+    cache = make_cache(k, v) if with_cache else None
+    got = oracle.window_step(q, k, v, cache)
+    for c in range(n):
+        rows = 2 * L if c + 1 < n else L
+        np.testing.assert_allclose(got[c].reshape(2 * L, H, D)[:rows],
+                                   np.broadcast_to(v[0, 0], (rows, H, D)), rtol=0, atol=1e-12)
+
+
+def test_window_zero_query_is_mean_over_window():
+    n, L, H, D = 4, 3, 1, 2
+    k, v = rand((n, L, H, D), 81), rand((n, L, H, D), 82)
+    q = np.zeros((n, L, H, D))
+    got = oracle.window_step(q, k, v, None)
+    for c in range(n):
+        keys = v[max(c - 1, 0): min(c + 2, n)].reshape(-1, H, D)
+        rows = 2 * L if c + 1 < n else L
+        np.testing.assert_allclose(got[c].reshape(2 * L, H, D)[:rows],
+                                   np.broadcast_to(keys.mean(0), (rows, H, D)), rtol=0,
+                                   atol=1e-12)
+
+
+def test_window_rows_match_window_step():
+    n, L, H, D = 3, 5, 2, 4
+    q, k, v = rand((n, L, H, D), 91), rand((n, L, H, D), 92), rand((n, L, H, D), 93)
+    cache = make_cache(k, v)
+    full = oracle.window_step(q, k, v, cache)
+    rows = [(0, 1, 0), (0, 0, 7), (1, 1, 9), (2, 0, 4), (1, 0, 5)]
+    got = oracle.window_rows(q, k, v, cache, rows)
+    for i, (c, h, r) in enumerate(rows):
+        np.testing.assert_array_equal(got[i], full[c, r // L, r % L, h])
+
+
+@pytest.mark.parametrize("L,n", [(1, 1), (3, 4), (7, 2), (16, 5)])
+def test_window_index_map_matches_mask_enumeration(L, n):
+    for c in range(n):
+        src, ch, row = oracle.window_index_map(L, n, c)
+        exp = [(oracle.SRC_PRED, c - 1, r) for r in range(L)] if c >= 1 else []
+        exp += [(oracle.SRC_OWN, cc, r) for cc in (c, c + 1) if cc < n for r in range(L)]
+        assert list(zip(src.tolist(), ch.tolist(), row.tolist())) == exp
+        assert oracle.window_kv_set_size(L, n, c) == len(exp)
+        assert oracle.window_q_rows(L, n, c) == (2 * L if c + 1 < n else L)

@@ -69,6 +69,14 @@ def load_library():
     lib.chunkattn_plan_debug.argtypes = [i32, i32, i32, i32, i32, vp, i64, ctypes.POINTER(i64)]
     lib.chunkattn_plan_device.restype = i32
     lib.chunkattn_plan_device.argtypes = [vp, i32, i32, i32, vp, i64, vp]
+    lib.chunkattn_window_step.restype = i32
+    lib.chunkattn_window_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
+    lib.chunkattn_validate_window_step.restype = i32
+    lib.chunkattn_validate_window_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                                   i32]
+    lib.chunkattn_window_plan_debug.restype = i32
+    lib.chunkattn_window_plan_debug.argtypes = [i32, i32, i32, i32, i32, vp, i64,
+                                                ctypes.POINTER(i64)]
     lib.chunkattn_ctx_xcd_count.restype = i32
     lib.chunkattn_ctx_xcd_count.argtypes = [vp]
     _lib = lib
@@ -172,18 +180,7 @@ def queue_step(q, k, v, kv_cache=None, out=None, scale=None, stream=None, ctx=No
     of chunk c-1); None reads chunk c-1 from k/v in place.  Returns `out`.
     """
     import torch
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("chunkattn.queue_step: q, k, v must all be [n, L, H, D]")
-    n, L, H, D = q.shape
-    for name, t in (("k", k), ("v", v)):
-        _require(t, name, q.device)
-        if t.dtype != q.dtype:
-            raise TypeError(f"chunkattn.queue_step: {name} dtype {t.dtype} != q dtype {q.dtype}")
-    _require(q, "q", q.device)
-    if kv_cache is not None:
-        _require(kv_cache, "kv_cache", q.device)
-        if kv_cache.shape != (n, 2, L, H, D) or kv_cache.dtype != q.dtype:
-            raise ValueError("chunkattn.queue_step: kv_cache must be [n, 2, L, H, D] of q's dtype")
+    n, L, H, D = _queue_args("queue_step", q, k, v, kv_cache)
     if out is None:
         out = torch.empty_like(q)
     else:
@@ -193,6 +190,47 @@ def queue_step(q, k, v, kv_cache=None, out=None, scale=None, stream=None, ctx=No
     scale = D ** -0.5 if scale is None else float(scale)
     ctx = ctx or create(q.device.index or 0)
     rc = load_library().chunkattn_queue_step(
+        ctx.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_cache), _ptr(out), L, n, H, D, scale,
+        _dtype_code(q), _stream(q, stream))
+    _check(rc, ctx.handle)
+    return out
+
+
+def _queue_args(fn, q, k, v, kv_cache):
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"chunkattn.{fn}: q, k, v must all be [n, L, H, D]")
+    n, L, H, D = q.shape
+    _require(q, "q", q.device)
+    for name, t in (("k", k), ("v", v)):
+        _require(t, name, q.device)
+        if t.dtype != q.dtype:
+            raise TypeError(f"chunkattn.{fn}: {name} dtype {t.dtype} != q dtype {q.dtype}")
+    if kv_cache is not None:
+        _require(kv_cache, "kv_cache", q.device)
+        if kv_cache.shape != (n, 2, L, H, D) or kv_cache.dtype != q.dtype:
+            raise ValueError(f"chunkattn.{fn}: kv_cache must be [n, 2, L, H, D] of q's dtype")
+    return n, L, H, D
+
+
+def window_step(q, k, v, kv_cache=None, out=None, scale=None, stream=None, ctx=None):
+    """One window step: window c's queries (chunks c and c+1) attend over
+    [chunk c-1's cached K/V ; own K/V of chunks c and c+1].
+
+    q, k, v, kv_cache as for queue_step.  Returns `out`, [n, 2, L, H, D]:
+    out[c, 0] = window c's rows of chunk c, out[c, 1] = its rows of chunk c+1
+    (out[n-1, 1] is left as it was).
+    """
+    import torch
+    n, L, H, D = _queue_args("window_step", q, k, v, kv_cache)
+    if out is None:
+        out = torch.empty((n, 2, L, H, D), dtype=q.dtype, device=q.device)
+    else:
+        _require(out, "out", q.device)
+        if out.shape != (n, 2, L, H, D) or out.dtype != q.dtype:
+            raise ValueError("chunkattn.window_step: out must be [n, 2, L, H, D] of q's dtype")
+    scale = D ** -0.5 if scale is None else float(scale)
+    ctx = ctx or create(q.device.index or 0)
+    rc = load_library().chunkattn_window_step(
         ctx.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_cache), _ptr(out), L, n, H, D, scale,
         _dtype_code(q), _stream(q, stream))
     _check(rc, ctx.handle)
@@ -246,6 +284,20 @@ def plan_debug(chunk_len: int, n_chunks: int, heads: int, n_xcd: int = 8,
     return items
 
 
+def window_plan_debug(chunk_len: int, n_chunks: int, heads: int, n_xcd: int = 8,
+                      block_rows: int = 0) -> np.ndarray:
+    """The window-step launch plan computed on the host, [n_items, 7] int32."""
+    lib = load_library()
+    n = ctypes.c_longlong()
+    _check(lib.chunkattn_window_plan_debug(chunk_len, n_chunks, heads, n_xcd, block_rows, None,
+                                           0, ctypes.byref(n)))
+    items = np.zeros((n.value, 7), np.int32)
+    _check(lib.chunkattn_window_plan_debug(chunk_len, n_chunks, heads, n_xcd, block_rows,
+                                           items.ctypes.data_as(ctypes.c_void_p), n.value,
+                                           ctypes.byref(n)))
+    return items
+
+
 def plan_device(chunk_len: int, n_chunks: int, heads: int, device: int = 0, ctx=None):
     """The same plan as decoded by the device kernel, [n_items, 7] int32 (GPU)."""
     import torch
@@ -277,4 +329,13 @@ def validate_full(q_ptr, k_ptr, v_ptr, out_ptr, batch, lq, lkv, kv_batch_stride,
     lib = load_library()
     rc = lib.chunkattn_validate_full(q_ptr, k_ptr, v_ptr, out_ptr, batch, lq, lkv,
                                      kv_batch_stride, heads, head_dim, scale, dtype)
+    return rc, lib.chunkattn_last_error(None).decode()
+
+
+def validate_window_step(q_ptr, k_ptr, v_ptr, cache_ptr, out_ptr, chunk_len, n_chunks, heads,
+                         head_dim, scale, dtype):
+    """(status, message) of the device-free argument checks of window_step."""
+    lib = load_library()
+    rc = lib.chunkattn_validate_window_step(q_ptr, k_ptr, v_ptr, cache_ptr, out_ptr, chunk_len,
+                                            n_chunks, heads, head_dim, scale, dtype)
     return rc, lib.chunkattn_last_error(None).decode()

@@ -14,7 +14,7 @@ from dataclasses import dataclass, field
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "queue" or "full"
+    kind: str                 # "queue", "window" or "full"
     n: int                    # chunks (queue) or batch (full)
     L: int                    # tokens per chunk (queue) or Lq (full)
     H: int
@@ -39,6 +39,14 @@ class Workload:
                 return 0.0
             kv_rows = self.L * self.L + (self.n - 1) * self.L * 2 * self.L
             return 4.0 * kv_rows * self.D * self.H
+        if self.kind == "window":
+            # window c: queries of chunks c and c+1 over chunks c-1, c, c+1
+            pairs = 0
+            for c in range(self.n):
+                q_chunks = 2 if c + 1 < self.n else 1
+                kv_chunks = 1 + (c >= 1) + (c + 1 < self.n)
+                pairs += q_chunks * kv_chunks
+            return 4.0 * pairs * self.L * self.L * self.D * self.H
         return 4.0 * self.n * self.L * self.lkv * self.D * self.H
 
     def nominal_flops(self) -> float:
@@ -69,6 +77,10 @@ WORKLOADS = {
                        k_rho=0.9, v_rho=0.9, n_text=512, seed=4, grid=(4, 45, 80),
                        note="16 chunks x (4 frames x 45x80), K and V AR(1) rho 0.9, "
                             "plus cross-attention to 512 shared text tokens"),
+    "win14b": Workload("win14b", "window", n=8, L=6240, H=40, D=128, dtype="bf16",
+                       k_rho=0.9, seed=5, grid=(4, 30, 52),
+                       note="the 40-head queue in the three-chunk window form: window c's "
+                            "queries are chunks c and c+1, its keys chunks c-1 (cached), c, c+1"),
 }
 
 # The timed workload: the 40-head, 480p-latent queue step.

@@ -73,7 +73,8 @@ struct KernelArgs {
   const void* pk;     // predecessor K: entry b at pk + (b - pred_shift)*p_bstride
   const void* pv;
   void* o;
-  int64_t q_bstride;  // elements between batch entries of q and out
+  int64_t q_bstride;  // elements between batch entries of q
+  int64_t o_bstride;  // elements between batch entries of out
   int64_t kv_bstride;
   int64_t p_bstride;
   int pred_shift;
@@ -237,7 +238,7 @@ __device__ __forceinline__ void attn_item_sync(const KernelArgs& a, const Item& 
 
   // ---- Q fragment: B operand of S^T = K.Q^T, one query row per lane column
   const int qrow = it.q0 + wave * 32 + l32;
-  const bool qvalid = qrow < a.plan.lq;
+  const bool qvalid = wave * 32 + l32 < it.q_rows;
   u32x4_t qf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
@@ -522,7 +523,7 @@ __device__ __forceinline__ void attn_item_sync(const KernelArgs& a, const Item& 
       for (int i = 0; i < 16; ++i) acc += oacc[db][i];
     if (__syncthreads_or(!__builtin_isfinite(acc))) {
       if (tid == 0)
-        static_cast<T*>(a.o)[it.b * a.q_bstride + (int64_t)it.q0 * rs + (int64_t)it.h * D] =
+        static_cast<T*>(a.o)[it.b * a.o_bstride + (int64_t)it.q0 * rs + (int64_t)it.h * D] =
             overflow_marker<T>();
       return;
     }
@@ -530,7 +531,7 @@ __device__ __forceinline__ void attn_item_sync(const KernelArgs& a, const Item& 
   const float l_tot = l_half + other_half(l_half);
   const float inv = 1.0f / l_tot;
   if (qvalid) {
-    T* ob = static_cast<T*>(a.o) + it.b * a.q_bstride + (int64_t)qrow * rs + (int64_t)it.h * D;
+    T* ob = static_cast<T*>(a.o) + it.b * a.o_bstride + (int64_t)qrow * rs + (int64_t)it.h * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -557,7 +558,7 @@ template <int D, typename T, int W>
 __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_recheck(KernelArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const Item it = decode(a.plan, slot_to_work(blockIdx.x, a.plan.n_items, a.plan.n_xcd));
-  const T first = static_cast<const T*>(a.o)[it.b * a.q_bstride + (int64_t)it.q0 * a.row_stride +
+  const T first = static_cast<const T*>(a.o)[it.b * a.o_bstride + (int64_t)it.q0 * a.row_stride +
                                               (int64_t)it.h * D];
   if (!__builtin_isnan((float)first)) return;
   attn_item_sync<D, T, W, false>(a, it, smem);

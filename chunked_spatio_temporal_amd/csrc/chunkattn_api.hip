@@ -67,16 +67,19 @@ int check_common(std::string* err, int heads, int head_dim, float scale, int dty
 // inside int64 and every row index of the kernel inside int32.
 constexpr long double kMaxElems = 4.0e18L;
 
+// Queue step (window = false) and window step (window = true: out holds two
+// chunks' rows per window, a work item walks up to 3 * chunk_len key rows).
 int validate_queue(std::string* err, const void* q, const void* k, const void* v,
                    const void* kv_cache, const void* out, int L, int n, int heads, int head_dim,
-                   float scale, int dtype) {
+                   float scale, int dtype, bool window = false) {
   int rc = check_common(err, heads, head_dim, scale, dtype);
   if (rc) return rc;
   if (L < 0 || n < 0)
     return set_err(err, CHUNKATTN_EINVAL, "chunk_len (%d) and n_chunks (%d) must be >= 0", L, n);
   if (L == 0 || n == 0) return CHUNKATTN_OK;
-  if (L > (1 << 30))
-    return set_err(err, CHUNKATTN_EUNSUPPORTED, "chunk_len %d too large (max 2^30)", L);
+  const int max_log2 = window ? 29 : 30;
+  if (L > (1 << max_log2))
+    return set_err(err, CHUNKATTN_EUNSUPPORTED, "chunk_len %d too large (max 2^%d)", L, max_log2);
   const long double elems = (long double)n * L * heads * head_dim;
   if (elems * 2 > kMaxElems)
     return set_err(err, CHUNKATTN_EINVAL, "tensor size overflows 64-bit offsets");
@@ -88,11 +91,13 @@ int validate_queue(std::string* err, const void* q, const void* k, const void* v
       (kv_cache && !aligned16(kv_cache)))
     return set_err(err, CHUNKATTN_EINVAL, "tensor pointers must be 16-byte aligned");
   const size_t bytes = (size_t)elems * elem_size(dtype);
-  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
-      overlaps(out, bytes, v, bytes) || (kv_cache && overlaps(out, bytes, kv_cache, 2 * bytes)))
+  const size_t obytes = window ? 2 * bytes : bytes;
+  if (overlaps(out, obytes, q, bytes) || overlaps(out, obytes, k, bytes) ||
+      overlaps(out, obytes, v, bytes) || (kv_cache && overlaps(out, obytes, kv_cache, 2 * bytes)))
     return set_err(err, CHUNKATTN_EINVAL, "out overlaps an input tensor");
+  const long double q_rows = window ? 2.0L * L : (long double)L;
   const long double items =
-      (long double)n * heads * ((L + kMinBlockRows - 1) / kMinBlockRows);
+      (long double)n * heads * ((long long)((q_rows + kMinBlockRows - 1) / kMinBlockRows));
   if (items > 2147483647.0L)
     return set_err(err, CHUNKATTN_EUNSUPPORTED, "too many work items for one launch");
   return CHUNKATTN_OK;
@@ -216,6 +221,13 @@ int run(chunkattn_ctx* ctx, const KernelArgs& a, int head_dim, int dtype, void* 
   return CHUNKATTN_OK;
 }
 
+// Plan of the window step: entry c = window c, queries = 2L rows starting at
+// chunk c (L for the last window), own rows = chunks c and c+1 (L for the
+// last), predecessor = chunk c-1 for c >= 1.
+Plan window_plan(int L, int n, int heads, int bm, int n_xcd) {
+  return chunkattn::make_plan(n, 1, heads, 2 * L, 2 * L, L, bm, n_xcd, L, L);
+}
+
 }  // namespace
 
 extern "C" {
@@ -302,6 +314,7 @@ int chunkattn_queue_step(chunkattn_ctx* ctx, const void* q, const void* k, const
   a.v = v;
   a.o = out;
   a.q_bstride = per_chunk;
+  a.o_bstride = per_chunk;
   a.kv_bstride = per_chunk;
   if (kv_cache) {
     a.pk = kv_cache;
@@ -339,12 +352,87 @@ int chunkattn_full(chunkattn_ctx* ctx, const void* q, const void* k, const void*
   a.pv = nullptr;
   a.o = out;
   a.q_bstride = (int64_t)lq * heads * head_dim;
+  a.o_bstride = a.q_bstride;
   a.kv_bstride = kv_batch_stride;
   a.p_bstride = 0;
   a.pred_shift = 0;
   a.row_stride = heads * head_dim;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   return run(ctx, a, head_dim, dtype, hip_stream);
+}
+
+int chunkattn_validate_window_step(const void* q, const void* k, const void* v,
+                                   const void* kv_cache, const void* out, int chunk_len,
+                                   int n_chunks, int heads, int head_dim, float scale,
+                                   int dtype) {
+  g_thread_err.clear();
+  return validate_queue(&g_thread_err, q, k, v, kv_cache, out, chunk_len, n_chunks, heads,
+                        head_dim, scale, dtype, true);
+}
+
+int chunkattn_window_step(chunkattn_ctx* ctx, const void* q, const void* k, const void* v,
+                          const void* kv_cache, void* out, int chunk_len, int n_chunks,
+                          int heads, int head_dim, float scale, int dtype, void* hip_stream) {
+  if (!ctx) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "ctx must be non-NULL");
+  int rc = validate_queue(&ctx->err, q, k, v, kv_cache, out, chunk_len, n_chunks, heads,
+                          head_dim, scale, dtype, true);
+  if (rc) return rc;
+  if (chunk_len == 0 || n_chunks == 0) {
+    ctx->err.clear();
+    return CHUNKATTN_OK;
+  }
+  const int64_t per_chunk = (int64_t)chunk_len * heads * head_dim;
+  const size_t es = elem_size(dtype);
+  KernelArgs a;
+  a.plan = window_plan(chunk_len, n_chunks, heads, 32 * ctx->waves, ctx->n_xcd);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.q_bstride = per_chunk;      // window c's queries start at chunk c
+  a.o_bstride = 2 * per_chunk;  // out[c] = [2][L][H][D]
+  a.kv_bstride = per_chunk;     // own rows start at chunk c
+  if (kv_cache) {
+    a.pk = kv_cache;
+    a.pv = static_cast<const unsigned char*>(kv_cache) + (size_t)per_chunk * es;
+    a.p_bstride = 2 * per_chunk;
+    a.pred_shift = 0;
+  } else {
+    a.pk = k;
+    a.pv = v;
+    a.p_bstride = per_chunk;
+    a.pred_shift = 1;
+  }
+  a.row_stride = heads * head_dim;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return run(ctx, a, head_dim, dtype, hip_stream);
+}
+
+int chunkattn_window_plan_debug(int chunk_len, int n_chunks, int heads, int n_xcd,
+                                int block_rows, int* items, long long cap, long long* n_items) {
+  g_thread_err.clear();
+  if (!n_items) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "n_items must be non-NULL");
+  if (block_rows == 0) block_rows = 32 * kDefaultWaves;
+  if (chunk_len < 0 || n_chunks < 0 || heads < 1 || cap < 0 || (cap > 0 && !items) ||
+      (block_rows != 128 && block_rows != 256))
+    return set_err(&g_thread_err, CHUNKATTN_EINVAL, "bad window_plan_debug arguments");
+  *n_items = 0;
+  if (chunk_len == 0 || n_chunks == 0) return CHUNKATTN_OK;
+  const Plan p = window_plan(chunk_len, n_chunks, heads, block_rows, n_xcd);
+  *n_items = p.n_items;
+  for (int64_t slot = 0; slot < p.n_items && slot < cap; ++slot) {
+    const chunkattn::Item it =
+        chunkattn::decode(p, chunkattn::slot_to_work(slot, p.n_items, p.n_xcd));
+    int* r = items + slot * 7;
+    r[0] = it.b;
+    r[1] = it.h;
+    r[2] = it.q0;
+    r[3] = it.q_rows;
+    r[4] = it.pred_rows > 0 ? it.b - 1 : -1;
+    r[5] = it.pred_rows;
+    r[6] = it.own_rows;
+  }
+  return CHUNKATTN_OK;
 }
 
 const char* chunkattn_status_string(int status) {

@@ -7,9 +7,12 @@
 // chunk processed just before, DualParal write-up section 三), j >= pred reads
 // row j - pred of the item's own K/V.  Nothing is concatenated in memory.
 //
+// The last batch entry may have fewer query and own rows than the others
+// (lq_last, lown_last): the last window of a window step has no next chunk.
+//
 // Order.  Items of batch entries that have a predecessor (chunks 1..n-1 of a
-// queue step) come first, because they walk twice the key rows; chunk 0, which
-// has none, fills the tail of the launch.  Within a group the order is
+// queue step) come first, because they walk the most key rows; entries without
+// one (chunk 0) fill the tail of the launch.  Within a group the order is
 // (b, h, t) with t fastest, so consecutive items share one chunk/head's K/V.
 //
 // Die-aware launch order.  Workgroup ids are handed to the accelerator dies
@@ -37,6 +40,9 @@ struct Plan {
   int lpred;       // predecessor rows (entries b >= first_pred)
   int bm;          // query rows per work item
   int n_qtiles;    // ceil(lq / bm)
+  int lq_last;     // query rows of the last entry (b = n_batch - 1)
+  int lown_last;   // own key/value rows of the last entry
+  int n_qtiles_last;
   int n_xcd;       // dies for the launch-order renumbering (>= 1)
   int64_t n_items;
   int64_t n_items_pred;  // items of entries with a predecessor (scheduled first)
@@ -47,7 +53,7 @@ struct Item {
 };
 
 CA_HD Plan make_plan(int n_batch, int first_pred, int heads, int lq, int lown, int lpred,
-                     int bm, int n_xcd) {
+                     int bm, int n_xcd, int lq_last, int lown_last) {
   Plan p;
   p.n_batch = n_batch;
   p.first_pred = first_pred < n_batch ? first_pred : n_batch;
@@ -57,11 +63,21 @@ CA_HD Plan make_plan(int n_batch, int first_pred, int heads, int lq, int lown, i
   p.lpred = lpred;
   p.bm = bm;
   p.n_qtiles = (lq + bm - 1) / bm;
+  p.lq_last = lq_last;
+  p.lown_last = lown_last;
+  p.n_qtiles_last = (lq_last + bm - 1) / bm;
   p.n_xcd = n_xcd < 1 ? 1 : n_xcd;
   const int64_t per_entry = (int64_t)heads * p.n_qtiles;
-  p.n_items = (int64_t)n_batch * per_entry;
-  p.n_items_pred = (int64_t)(n_batch - p.first_pred) * per_entry;
+  const int64_t per_last = (int64_t)heads * p.n_qtiles_last;
+  p.n_items = n_batch > 0 ? (int64_t)(n_batch - 1) * per_entry + per_last : 0;
+  const int n_pred = n_batch - p.first_pred;  // the last entry is among them if n_pred > 0
+  p.n_items_pred = n_pred > 0 ? (int64_t)(n_pred - 1) * per_entry + per_last : 0;
   return p;
+}
+// Every entry the same size.
+CA_HD Plan make_plan(int n_batch, int first_pred, int heads, int lq, int lown, int lpred,
+                     int bm, int n_xcd) {
+  return make_plan(n_batch, first_pred, heads, lq, lown, lpred, bm, n_xcd, lq, lown);
 }
 
 // Launch slot (workgroup id) -> work index.  A bijection on [0, n): die x
@@ -77,25 +93,41 @@ CA_HD int64_t slot_to_work(int64_t slot, int64_t n, int n_xcd) {
 }
 
 CA_HD Item decode(const Plan& p, int64_t w) {
+  // group: entries [first_pred, n_batch) first, then [0, first_pred)
+  int64_t idx = w;
+  int b0 = p.first_pred, count = p.n_batch - p.first_pred;
+  if (w >= p.n_items_pred) {
+    idx = w - p.n_items_pred;
+    b0 = 0;
+    count = p.first_pred;
+  }
+  // the group's entries are regular except the last entry of the queue
+  const int regular = b0 + count == p.n_batch ? count - 1 : count;
   const int64_t per_entry = (int64_t)p.heads * p.n_qtiles;
   int64_t b, rem;
-  if (w < p.n_items_pred) {
-    b = p.first_pred + w / per_entry;
-    rem = w % per_entry;
+  int nq, lq, lown;
+  if (idx < (int64_t)regular * per_entry) {
+    b = b0 + idx / per_entry;
+    rem = idx % per_entry;
+    nq = p.n_qtiles;
+    lq = p.lq;
+    lown = p.lown;
   } else {
-    const int64_t w2 = w - p.n_items_pred;
-    b = w2 / per_entry;
-    rem = w2 % per_entry;
+    b = p.n_batch - 1;
+    rem = idx - (int64_t)regular * per_entry;
+    nq = p.n_qtiles_last;
+    lq = p.lq_last;
+    lown = p.lown_last;
   }
   Item it;
   it.b = (int)b;
-  it.h = (int)(rem / p.n_qtiles);
-  const int t = (int)(rem % p.n_qtiles);
+  it.h = (int)(rem / nq);
+  const int t = (int)(rem % nq);
   it.q0 = t * p.bm;
-  const int left = p.lq - it.q0;
+  const int left = lq - it.q0;
   it.q_rows = left < p.bm ? left : p.bm;
   it.pred_rows = b >= p.first_pred ? p.lpred : 0;
-  it.own_rows = p.lown;
+  it.own_rows = lown;
   return it;
 }
 

@@ -114,6 +114,30 @@ int chunkattn_queue_step(chunkattn_ctx *ctx, const void *q, const void *k, const
                          int heads, int head_dim, float scale, int dtype, void *hip_stream);
 
 /*
+ * One window step, the form the feature cache is introduced for in the
+ * DualParal write-up (section 三): processing the window [B_{i-1}, B_i] of
+ * two neighbouring chunks reuses the cached self-attention K/V of B_{i+1},
+ * the chunk processed just before.  With chunks in processing order, window c
+ * (c in [0, n_chunks)) is centred on chunk c:
+ *   queries  the rows of chunk c, then of chunk c+1 (2 * chunk_len rows; only
+ *            chunk c's for the last window, c = n_chunks-1);
+ *   keys/values  W_c = [chunk c-1's K/V from the cache (c >= 1)]
+ *            ++ [own K/V of chunk c] ++ [own K/V of chunk c+1 (c+1 < n_chunks)];
+ * plain softmax attention of every query row over W_c, every head, in one
+ * launch on hip_stream.
+ *
+ *   q, k, v, kv_cache  as for chunkattn_queue_step (kv_cache slot c holds
+ *            chunk c-1's K then V; NULL reads chunk c-1 in place).
+ *   out      [n_chunks][2][chunk_len][heads][head_dim]: out[c][0] = window c's
+ *            rows of chunk c, out[c][1] = its rows of chunk c+1.  out[n-1][1]
+ *            is not written.  Must not overlap any input.
+ *   chunk_len <= 2^29; other arguments as for chunkattn_queue_step.
+ */
+int chunkattn_window_step(chunkattn_ctx *ctx, const void *q, const void *k, const void *v,
+                          const void *kv_cache, void *out, int chunk_len, int n_chunks,
+                          int heads, int head_dim, float scale, int dtype, void *hip_stream);
+
+/*
  * Non-chunked attention: every query row of batch item b attends over all lkv
  * rows of its K/V (the full-sequence attention the chunked form avoids, and
  * the per-chunk cross-attention to text tokens, which uses no cache).
@@ -141,6 +165,10 @@ int chunkattn_validate_queue_step(const void *q, const void *k, const void *v,
 int chunkattn_validate_full(const void *q, const void *k, const void *v, const void *out,
                             int batch, int lq, int lkv, long long kv_batch_stride, int heads,
                             int head_dim, float scale, int dtype);
+int chunkattn_validate_window_step(const void *q, const void *k, const void *v,
+                                   const void *kv_cache, const void *out, int chunk_len,
+                                   int n_chunks, int heads, int head_dim, float scale,
+                                   int dtype);
 
 /* Static description of a status code. */
 const char *chunkattn_status_string(int status);
@@ -165,6 +193,15 @@ const char *chunkattn_last_error(const chunkattn_ctx *ctx);
  */
 int chunkattn_plan_debug(int chunk_len, int n_chunks, int heads, int n_xcd, int block_rows,
                          int *items, long long cap, long long *n_items);
+
+/*
+ * The work plan of a window step, as chunkattn_plan_debug: the first field is
+ * the window c; q_row0/q_rows index window c's 2 * chunk_len query rows (rows
+ * >= chunk_len are chunk c+1's); own_rows is 2 * chunk_len (chunk_len for the
+ * last window), read from chunk c onwards.
+ */
+int chunkattn_window_plan_debug(int chunk_len, int n_chunks, int heads, int n_xcd,
+                                int block_rows, int *items, long long cap, long long *n_items);
 
 /*
  * The same plan as decoded on the device by the attention kernel's own decode

@@ -102,6 +102,38 @@ def test_validate_full():
     assert vf(out=3 * P)[0] == ca.EINVAL
 
 
+def vw(**kw):
+    a = dict(q=P, k=2 * P, v=3 * P, cache=None, out=4 * P, L=16, n=2, H=2, D=128,
+             scale=0.1, dtype=ca.BF16)
+    a.update(kw)
+    return ca.validate_window_step(a["q"], a["k"], a["v"], a["cache"], a["out"], a["L"],
+                                   a["n"], a["H"], a["D"], a["scale"], a["dtype"])
+
+
+def test_validate_window_step():
+    assert vw()[0] == ca.OK
+    assert vw(cache=8 * P)[0] == ca.OK
+    assert vw(n=0, q=None, k=None, v=None, out=None)[0] == ca.OK
+    # out holds two chunks' rows per window: [P - 16 KiB, P + 16 KiB) overlaps q,
+    # while the queue step's out of half that size ends where q starts
+    below_q = P - 16 * 2 * 128 * 2 * 2
+    assert vq(out=below_q)[0] == ca.OK
+    assert vw(out=below_q)[0] == ca.EINVAL
+    # a window walks up to 3 * chunk_len key rows: chunk_len is capped at 2^29
+    far = dict(q=1 << 40, k=2 << 40, v=3 << 40, out=4 << 40, n=1, H=1, D=64)
+    assert vq(L=(1 << 29) + 1, **far)[0] == ca.OK
+    assert vw(L=(1 << 29) + 1, **far)[0] == ca.EUNSUPPORTED
+    assert vw(L=1 << 29, **far)[0] == ca.OK
+    for kw, code in [(dict(D=96), ca.EUNSUPPORTED), (dict(scale=-1.0), ca.EINVAL),
+                     (dict(k=P + 2), ca.EINVAL), (dict(out=P), ca.EINVAL)]:
+        assert vw(**kw)[0] == code
+
+
+def test_window_step_without_context_is_rejected():
+    assert lib.chunkattn_window_step(None, P, 2 * P, 3 * P, None, 4 * P, 16, 2, 2, 128,
+                                     ctypes.c_float(0.1), 0, None) == ca.EINVAL
+
+
 def test_queue_step_without_context_is_rejected():
     assert lib.chunkattn_queue_step(None, P, 2 * P, 3 * P, None, 4 * P, 16, 2, 2, 128,
                                     ctypes.c_float(0.1), 0, None) == ca.EINVAL
@@ -149,6 +181,50 @@ def test_plan_matches_oracle_index_map(L, n, H, xcd, bm):
         np.testing.assert_array_equal(plan_src, src)
         np.testing.assert_array_equal(plan_ch, ch)
         np.testing.assert_array_equal(plan_row, row)
+
+
+@pytest.mark.parametrize("bm", [128, 256])
+@pytest.mark.parametrize("L,n,H,xcd", [(128, 4, 2, 8), (97, 5, 3, 8), (1, 1, 1, 8),
+                                       (300, 3, 7, 1), (6240, 8, 40, 8), (200, 2, 3, 3),
+                                       (64, 1, 2, 8)])
+def test_window_plan_matches_oracle_window_map(L, n, H, xcd, bm):
+    items = ca.window_plan_debug(L, n, H, xcd, bm)
+    c, h, q0, qr, pc, pr, orows = items.T.astype(np.int64)
+    # every (window, head, query row) exactly once: 2L rows per window, L for the last
+    expect = sum(H * -(-oracle.window_q_rows(L, n, cc) // bm) for cc in range(n))
+    assert items.shape == (expect, 7)
+    covered = set()
+    for it in items:
+        for r in range(it[2], it[2] + it[3]):
+            covered.add((int(it[0]), int(it[1]), r))
+    assert len(covered) == sum(it[3] for it in items)
+    assert covered == {(cc, hh, r) for cc in range(n) for hh in range(H)
+                       for r in range(oracle.window_q_rows(L, n, cc))}
+    assert ((qr > 0) & (qr <= bm) & (q0 % bm == 0)).all()
+    # each item's key/value set is the oracle's window map, bit for bit: the own
+    # segment is read contiguously from chunk c (chunk c, then chunk c+1)
+    for cc in range(n):
+        kv = np.unique(items[c == cc][:, 4:7], axis=0)
+        assert kv.shape == (1, 3), "items of one window disagree on their key/value set"
+        pcc, prr, oww = kv[0]
+        src, ch, row = oracle.window_index_map(L, n, cc)
+        own = np.arange(oww)
+        np.testing.assert_array_equal(
+            np.r_[np.full(prr, oracle.SRC_PRED), np.full(oww, oracle.SRC_OWN)], src)
+        np.testing.assert_array_equal(np.r_[np.full(prr, pcc), cc + own // L], ch)
+        np.testing.assert_array_equal(np.r_[np.arange(prr), own % L], row)
+
+
+def test_window_plan_order_longest_first():
+    L, n, H, xcd = 6240, 8, 40, 8
+    items = ca.window_plan_debug(L, n, H, xcd)
+    bm = ca.block_rows()
+    nq, nq_last = -(-2 * L // bm), -(-L // bm)
+    by_work = items[np.argsort(_slot_to_work_reference(len(items), xcd))]
+    # windows 1..n-2 (three segments), the last window, then window 0
+    expect_c = np.r_[np.repeat(np.arange(1, n - 1), H * nq), np.full(H * nq_last, n - 1),
+                     np.zeros(H * nq, int)]
+    np.testing.assert_array_equal(by_work[:, 0], expect_c)
 
 
 def test_default_block_rows():

@@ -74,11 +74,14 @@ def main():
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
     t0 = time.time()
-    if w.kind == "queue":
+    if w.kind in ("queue", "window"):
         q, k, v = synth.queue_inputs(w.n, w.L, w.H, w.D, w.seed, device=dev, dtype=dt,
                                      k_rho=w.k_rho, v_rho=w.v_rho)
         cache = synth.build_cache(k, v)
-        out = torch.empty_like(q)
+        if w.kind == "queue":
+            out = torch.empty_like(q)
+        else:
+            out = torch.empty((w.n, 2, w.L, w.H, w.D), dtype=dt, device=dev)
         if w.n_text:
             qx = synth.cross_queries(w.n, w.L, w.H, w.D, w.seed, dev, dt)
             kt, vt = synth.text_inputs(w.n_text, w.H, w.D, w.seed, dev, dt)
@@ -100,6 +103,8 @@ def main():
     def dominant():
         if w.kind == "queue":
             ca.queue_step(q, k, v, cache, out=out, scale=w.scale, stream=stream, ctx=ctx)
+        elif w.kind == "window":
+            ca.window_step(q, k, v, cache, out=out, scale=w.scale, stream=stream, ctx=ctx)
         else:
             ca.full(q, k, v, out=out, scale=w.scale, stream=stream, ctx=ctx)
 
@@ -191,6 +196,8 @@ def main():
             "heads": w.H,
             "head_dim": w.D,
             "lkv": w.lkv if w.kind == "full" else None,
+            "window": ("queries of chunks c and c+1; keys of chunks c-1 (cached), c, c+1"
+                       if w.kind == "window" else None),
             "kv_cache": "separate buffer" if cache is not None else None,
             "text_tokens": w.n_text or None,
             "block_rows": ctx.block_rows,
@@ -238,6 +245,21 @@ def cpu_baseline(w, q, k, v, cache, seconds):
             return float(sum(4 * (2 * w.L if c >= 1 else w.L) * w.D for c in rows[:, 0]))
 
         run = lambda rows: oracle.queue_rows(qs, ks, vs, cs, rows, w.scale)
+    elif w.kind == "window":
+        # window 1 of the three-chunk sub-problem [0, 1, 2]: 2L query rows over
+        # 3L keys (the shape of every interior window)
+        sub = lambda t: t[0:3].cpu()
+        qs, ks, vs = sub(q), sub(k), sub(v)
+        cs = None if cache is None else sub(cache)
+
+        def rows_for(count):
+            return np.stack([np.ones(count, np.int64), rng.integers(0, w.H, count),
+                             rng.integers(0, 2 * w.L, count)], 1)
+
+        def flops(rows):
+            return float(len(rows) * 4 * 3 * w.L * w.D)
+
+        run = lambda rows: oracle.window_rows(qs, ks, vs, cs, rows, w.scale)
     else:
         qs, ks, vs = q.cpu(), k.cpu(), v.cpu()
 
@@ -250,11 +272,11 @@ def cpu_baseline(w, q, k, v, cache, seconds):
 
         run = lambda rows: oracle.full_rows(qs, ks, vs, rows, w.scale)
 
-    probe = rows_for(64)
+    probe = rows_for(512)
     t0 = time.perf_counter()
     run(probe)
     dt = time.perf_counter() - t0
-    count = int(max(64, min(200000, 64 * seconds / max(dt, 1e-6))))
+    count = int(max(512, min(400000, 512 * seconds / max(dt, 1e-6))))
     rows = rows_for(count)
     t0 = time.perf_counter()
     run(rows)
@@ -265,7 +287,8 @@ def cpu_baseline(w, q, k, v, cache, seconds):
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"{count} random query rows (all heads) of {w.name}, each over its full "
+        "sample": f"{count} random query rows (all heads) of {w.name}"
+                  f"{' interior windows' if w.kind == 'window' else ''}, each over its full "
                   f"key/value set; {dt:.1f} s; fp64",
         "queue_steps_per_s_extrapolated": round(tflops * 1e12 / w.self_flops(), 8),
         "cpu_model": _cpu_model(),

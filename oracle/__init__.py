@@ -22,6 +22,11 @@ Parity status of each entry point (what pins it, in tests/test_oracle_pins.py):
                            mask, single-chunk reduction to full attention,
                            constant-V and closed forms, golden fixtures
   window_index_map         pinned: brute-force enumeration of the window mask
+  ring_rows / ring_slot    pinned: the linear queue step on the chunks gathered
+                           from their slots, wrap-around closed forms
+  fifo.Fifo / fifo.run     pinned: the queue properties the page states (noise
+                           falls from tail to head, depth steps per chunk,
+                           arrival order kept, bounded length)
 """
 import ctypes
 import os
@@ -69,6 +74,11 @@ def _load():
     lib.oracle_window_rows.restype = i32
     lib.oracle_window_rows.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i64, dbl, vp, i64,
                                        vp]
+    lib.oracle_ring_slot.restype = i64
+    lib.oracle_ring_slot.argtypes = [i64, i64, i64]
+    lib.oracle_ring_rows.restype = i32
+    lib.oracle_ring_rows.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, vp,
+                                     i64, vp]
     lib.oracle_full_rows.restype = i32
     lib.oracle_full_rows.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl,
                                      vp, i64, vp]
@@ -271,4 +281,23 @@ def window_rows(q, k, v, kv_cache, rows, scale=None) -> np.ndarray:
                                     scale, _ptr(rows), rows.shape[0], _ptr(out))
     if rc != 0:
         raise RuntimeError(f"oracle_window_rows failed ({rc})")
+    return out
+
+
+def ring_slot(slots: int, tail_slot: int, c: int) -> int:
+    return int(_load().oracle_ring_slot(slots, tail_slot, c))
+
+
+def ring_rows(q, k, v, tail_slot, n_live, rows, scale=None) -> np.ndarray:
+    """Queue step over the n_live chunks of ring buffers q, k, v [S][L][H][D]
+    (chunk c in processing order in slot (tail_slot - c) mod S); rows is (N, 3)
+    of (chunk c, head, row).  Returns fp64 (N, D)."""
+    qa, ka, va, _, dt, (S, L, H, D) = _common(q, k, v, None)
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    rows = np.ascontiguousarray(np.asarray(rows, np.int64).reshape(-1, 3))
+    out = np.empty((rows.shape[0], D), np.float64)
+    rc = _load().oracle_ring_rows(dt, _ptr(qa), _ptr(ka), _ptr(va), S, tail_slot, n_live, L, H,
+                                  D, scale, _ptr(rows), rows.shape[0], _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"oracle_ring_rows failed ({rc})")
     return out

@@ -47,6 +47,15 @@
  * output of window c holds its 2L query rows: out[c][0] = chunk c's rows,
  * out[c][1] = chunk c+1's rows (absent for the last window).
  *
+ * Streaming queue (same page, section 二: new noisy chunks enter at the tail,
+ * clean ones leave at the head, the queue is processed from tail to head, so
+ * the video can grow without bound).  The chunks live in a ring of S slots;
+ * with the live chunks listed in processing order (c = 0 is the tail, the
+ * newest), chunk c sits in slot (tail - c) mod S, and its predecessor (chunk
+ * c-1, the next newer one, processed just before it) in slot
+ * (tail - c + 1) mod S, read in place.  Each live chunk then attends over R_c
+ * exactly as above.
+ *
  * Precision.  Every input element is widened exactly to fp64 (bf16 and fp32
  * both embed exactly); scores, exponentials, sums and the weighted sum are
  * fp64, the dot product summed in increasing dimension order.  Two passes per
@@ -57,6 +66,8 @@
  *   q, k, v, out      [n_chunks][L][H][D]
  *   kv_cache          [n_chunks][2][L][H][D]   (slot c: K of c-1, then V of c-1)
  *   window out        [n_chunks][2][L][H][D]   (window c: chunk c, then chunk c+1)
+ *   ring q, k, v, out [S][L][H][D]             (slot p; chunk c of the queue in
+ *                                               slot (tail - c) mod S)
  *   full attention    q/out [batch][Lq][H][D],  k/v batch b at b*kv_batch_stride,
  *                     each [Lkv][H][D]
  */
@@ -544,6 +555,75 @@ int oracle_window_rows(int dtype, const void *q, const void *k, const void *v,
                 src.map_row = map + 2 * max_nk;
                 attend_row(dtype, q, ((q_chunk * L + q_row) * H + h) * D, &src, nk, scale, s,
                            dst, NULL);
+            }
+        }
+        free(s);
+        free(map);
+    }
+    return bad ? -2 : 0;
+}
+
+/* ---- streaming queue over a ring of slots ----------------------------- */
+
+/* Slot of the queue's chunk c (processing order, c = 0 the tail). */
+int64_t oracle_ring_slot(int64_t slots, int64_t tail_slot, int64_t c)
+{
+    int64_t p = (tail_slot - c) % slots;
+    return p < 0 ? p + slots : p;
+}
+
+/*
+ * Queue step over the n_live chunks of a ring, selected rows (chunk c in
+ * processing order, head, row); out: n_rows x D.  The key/value set of chunk c
+ * is [the predecessor's rows (c >= 1)] ++ [its own rows], both read in place
+ * from their slots.
+ */
+int oracle_ring_rows(int dtype, const void *q, const void *k, const void *v, int64_t slots,
+                     int64_t tail_slot, int64_t n_live, int64_t L, int64_t H, int64_t D,
+                     double scale, const int64_t *rows, int64_t n_rows, double *out)
+{
+    if (slots <= 0 || n_live <= 0 || n_live > slots || tail_slot < 0 || tail_slot >= slots ||
+        L <= 0 || H <= 0 || D <= 0)
+        return -1;
+    for (int64_t i = 0; i < n_rows; ++i) {
+        int64_t c = rows[3 * i], h = rows[3 * i + 1], r = rows[3 * i + 2];
+        if (c < 0 || c >= n_live || h < 0 || h >= H || r < 0 || r >= L)
+            return -1;
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * 2 * L);
+        int64_t *map = (int64_t *)malloc(sizeof(int64_t) * 3 * 2 * L);
+        if (!s || !map) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t i = 0; i < n_rows; ++i) {
+                const int64_t c = rows[3 * i], h = rows[3 * i + 1], r = rows[3 * i + 2];
+                /* R_c as (source, slot, row): predecessor slot, then own slot */
+                int64_t nk = 0;
+                int64_t *src = map, *slot = map + 2 * L, *row = map + 4 * L;
+                if (c >= 1)
+                    for (int64_t j = 0; j < L; ++j, ++nk) {
+                        src[nk] = ORACLE_SRC_OWN;  /* read in place, not from a cache */
+                        slot[nk] = oracle_ring_slot(slots, tail_slot, c - 1);
+                        row[nk] = j;
+                    }
+                for (int64_t j = 0; j < L; ++j, ++nk) {
+                    src[nk] = ORACLE_SRC_OWN;
+                    slot[nk] = oracle_ring_slot(slots, tail_slot, c);
+                    row[nk] = j;
+                }
+                kv_source ks = queue_source(k, v, NULL, 0, h, L, H, D);
+                ks.window = 1;  /* explicit (source, chunk slot, row) list */
+                ks.map_src = src;
+                ks.map_chunk = slot;
+                ks.map_row = row;
+                const int64_t q_off =
+                    ((oracle_ring_slot(slots, tail_slot, c) * L + r) * H + h) * D;
+                attend_row(dtype, q, q_off, &ks, nk, scale, s, out + i * D, NULL);
             }
         }
         free(s);

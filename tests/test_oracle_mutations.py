@@ -40,6 +40,9 @@ MUTANTS = {
                                      "*ko = ((((c - 1) * 2 + 0) * L + row) * H + h) * D;"),
     "window_heads_mixed": ("*ko = ((chunk * L + row) * H + h) * D;",
                            "*ko = ((chunk * L + row) * H + 0) * D;"),
+    "ring_wrap_clamped": ("return p < 0 ? p + slots : p;", "return p < 0 ? 0 : p;"),
+    "ring_predecessor_older": ("slot[nk] = oracle_ring_slot(slots, tail_slot, c - 1);",
+                               "slot[nk] = oracle_ring_slot(slots, tail_slot, c + 1);"),
     "window_predecessor_dropped": ("if (c >= 1)\n        for (int64_t r = 0; r < chunk_len; ++r, ++j) {",
                                    "if (0)\n        for (int64_t r = 0; r < chunk_len; ++r, ++j) {"),
 }

@@ -481,3 +481,74 @@ def test_window_index_map_matches_mask_enumeration(L, n):
         assert list(zip(src.tolist(), ch.tolist(), row.tolist())) == exp
         assert oracle.window_kv_set_size(L, n, c) == len(exp)
         assert oracle.window_q_rows(L, n, c) == (2 * L if c + 1 < n else L)
+
+
+# --------------------------------------------------------------------------
+# streaming queue over a ring of slots (DualParal write-up, section 二)
+
+from oracle import fifo as fifo_sim  # noqa: E402
+
+
+@pytest.mark.parametrize("S,tail,n", [(5, 3, 4), (5, 1, 4), (4, 0, 4), (7, 6, 1), (3, 2, 3)])
+def test_ring_step_is_the_queue_step_on_gathered_chunks(S, tail, n):
+    L, H, D = 6, 2, 5
+    q, k, v = rand((S, L, H, D), 101), rand((S, L, H, D), 102), rand((S, L, H, D), 103)
+    order = [(tail - c) % S for c in range(n)]  # processing order, tail first
+    lin = oracle.queue_step(q[order], k[order], v[order], None, scale=0.6)
+    rows = [(c, h, r) for c in range(n) for h in range(H) for r in range(L)]
+    got = oracle.ring_rows(q, k, v, tail, n, rows, scale=0.6)
+    np.testing.assert_allclose(got, np.array([lin[c, r, h] for c, h, r in rows]), rtol=0,
+                               atol=1e-12)
+
+
+def test_ring_wraparound_closed_form():
+    """S = 3, tail in slot 0: chunk 0 is slot 0, chunk 1 slot 2 (wrapped), and
+    chunk 1's predecessor is chunk 0 in slot 0.  One token, D = 1, q = 1:
+    chunk 1 sees keys (slot 0: ln 3, slot 2: 0), weights (3/4, 1/4), values
+    (8, 4) -> 7; chunk 0 sees only its own key -> its value 8."""
+    q = np.ones((3, 1, 1, 1))
+    k = np.array([math.log(3.0), 50.0, 0.0]).reshape(3, 1, 1, 1)   # slot 1 unused
+    v = np.array([8.0, -100.0, 4.0]).reshape(3, 1, 1, 1)
+    got = oracle.ring_rows(q, k, v, 0, 2, [(0, 0, 0), (1, 0, 0)], scale=1.0)
+    np.testing.assert_allclose(got[:, 0], [8.0, 7.0], rtol=0, atol=1e-12)
+    assert [oracle.ring_slot(3, 0, c) for c in range(3)] == [0, 2, 1]
+
+
+def test_fifo_follows_the_page():
+    """Noise falls from tail to head (steps done rise), every chunk stays exactly
+    `depth` steps, chunks leave in arrival order, the queue never exceeds depth,
+    and live chunks always sit in distinct slots."""
+    total, S, depth = 11, 5, 4
+    sched = fifo_sim.run(total, S, depth)
+    assert len(sched) == total + depth - 1
+    entered, left = {}, []
+    for step, (pushed, live, popped) in enumerate(sched):
+        assert 1 <= len(live) <= depth
+        dones = [d for _, _, d in live]
+        assert dones == sorted(dones) and len(set(dones)) == len(dones)
+        assert len({s for _, s, _ in live}) == len(live)
+        assert [s for _, s, _ in live] == [(live[0][1] - c) % S for c in range(len(live))]
+        for g, _, d in live:
+            entered.setdefault(g, step - d)
+        if popped >= 0:
+            g_head = live[-1][0]
+            assert popped == g_head % S and step - entered[g_head] + 1 == depth
+            left.append(g_head)
+    assert left == list(range(total))
+
+
+def test_fifo_rejects_misuse():
+    f = fifo_sim.Fifo(4, 2)
+    with pytest.raises(ValueError):
+        f.step()
+    f.push()
+    f.push()
+    with pytest.raises(ValueError):
+        f.push()           # full
+    f.step()
+    with pytest.raises(ValueError):
+        f.pop()            # head has done 1 of 2 steps
+    f.step()
+    assert f.pop() == 0
+    with pytest.raises(ValueError):
+        fifo_sim.Fifo(3, 4)

@@ -77,6 +77,26 @@ def load_library():
     lib.chunkattn_window_plan_debug.restype = i32
     lib.chunkattn_window_plan_debug.argtypes = [i32, i32, i32, i32, i32, vp, i64,
                                                 ctypes.POINTER(i64)]
+    lib.chunkattn_ring_step.restype = i32
+    lib.chunkattn_ring_step.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                        i32, vp]
+    lib.chunkattn_validate_ring_step.restype = i32
+    lib.chunkattn_validate_ring_step.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                                 f32, i32]
+    lib.chunkattn_fifo_create.restype = i32
+    lib.chunkattn_fifo_create.argtypes = [ctypes.POINTER(vp), i32, i32]
+    lib.chunkattn_fifo_destroy.restype = i32
+    lib.chunkattn_fifo_destroy.argtypes = [vp]
+    lib.chunkattn_fifo_push.restype = i32
+    lib.chunkattn_fifo_push.argtypes = [vp, ctypes.POINTER(i32)]
+    lib.chunkattn_fifo_pop.restype = i32
+    lib.chunkattn_fifo_pop.argtypes = [vp, ctypes.POINTER(i32)]
+    lib.chunkattn_fifo_live.restype = i32
+    lib.chunkattn_fifo_live.argtypes = [vp, vp, vp, vp, i32, ctypes.POINTER(i32)]
+    lib.chunkattn_fifo_advance.restype = i32
+    lib.chunkattn_fifo_advance.argtypes = [vp]
+    lib.chunkattn_fifo_step.restype = i32
+    lib.chunkattn_fifo_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, i32, vp]
     lib.chunkattn_ctx_xcd_count.restype = i32
     lib.chunkattn_ctx_xcd_count.argtypes = [vp]
     _lib = lib
@@ -237,6 +257,96 @@ def window_step(q, k, v, kv_cache=None, out=None, scale=None, stream=None, ctx=N
     return out
 
 
+def _ring_args(fn, q_ring, k_ring, v_ring, out_ring):
+    if q_ring.dim() != 4 or k_ring.shape != q_ring.shape or v_ring.shape != q_ring.shape:
+        raise ValueError(f"chunkattn.{fn}: q, k, v rings must all be [slots, L, H, D]")
+    for name, t in (("q_ring", q_ring), ("k_ring", k_ring), ("v_ring", v_ring),
+                    ("out_ring", out_ring)):
+        _require(t, name, q_ring.device)
+        if t.dtype != q_ring.dtype:
+            raise TypeError(f"chunkattn.{fn}: {name} dtype {t.dtype} != {q_ring.dtype}")
+    if out_ring.shape != q_ring.shape:
+        raise ValueError(f"chunkattn.{fn}: out_ring must match q_ring")
+    return q_ring.shape
+
+
+def ring_step(q_ring, k_ring, v_ring, out_ring, tail_slot, n_live, scale=None, stream=None,
+              ctx=None):
+    """Queue step over the n_live chunks of ring buffers [slots, L, H, D]:
+    chunk c (tail first) in slot (tail_slot - c) mod slots attends over its
+    predecessor's slot (read in place) and its own.  Writes those slots of
+    out_ring; returns out_ring."""
+    S, L, H, D = _ring_args("ring_step", q_ring, k_ring, v_ring, out_ring)
+    scale = D ** -0.5 if scale is None else float(scale)
+    ctx = ctx or create(q_ring.device.index or 0)
+    rc = load_library().chunkattn_ring_step(
+        ctx.handle, _ptr(q_ring), _ptr(k_ring), _ptr(v_ring), _ptr(out_ring), S, int(tail_slot),
+        int(n_live), L, H, D, scale, _dtype_code(q_ring), _stream(q_ring, stream))
+    _check(rc, ctx.handle)
+    return out_ring
+
+
+class Fifo:
+    """The streaming chunk queue's host bookkeeping (C++ object behind the C
+    ABI): chunk g lives in slot g mod slots, each chunk stays `depth` steps."""
+
+    def __init__(self, slots: int, depth: int):
+        lib = load_library()
+        h = ctypes.c_void_p()
+        _check(lib.chunkattn_fifo_create(ctypes.byref(h), slots, depth))
+        self.handle = h
+        self.slots = slots
+        self.depth = depth
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and _lib is not None:
+            _lib.chunkattn_fifo_destroy(h)
+            self.handle = None
+
+    def push(self) -> int:
+        s = ctypes.c_int()
+        _check(load_library().chunkattn_fifo_push(self.handle, ctypes.byref(s)))
+        return s.value
+
+    def pop(self) -> int:
+        s = ctypes.c_int()
+        _check(load_library().chunkattn_fifo_pop(self.handle, ctypes.byref(s)))
+        return s.value
+
+    def live(self):
+        """[(chunk number, slot, steps done)] in processing order, tail first."""
+        lib = load_library()
+        n = ctypes.c_int()
+        _check(lib.chunkattn_fifo_live(self.handle, None, None, None, 0, ctypes.byref(n)))
+        ids = np.zeros(max(n.value, 1), np.int64)
+        slots = np.zeros(max(n.value, 1), np.int32)
+        done = np.zeros(max(n.value, 1), np.int32)
+        _check(lib.chunkattn_fifo_live(self.handle, ids.ctypes.data_as(ctypes.c_void_p),
+                                       slots.ctypes.data_as(ctypes.c_void_p),
+                                       done.ctypes.data_as(ctypes.c_void_p), n.value,
+                                       ctypes.byref(n)))
+        return [(int(ids[i]), int(slots[i]), int(done[i])) for i in range(n.value)]
+
+    def advance(self) -> None:
+        """Mark one step done for every live chunk (no launch)."""
+        _check(load_library().chunkattn_fifo_advance(self.handle))
+
+    def step(self, q_ring, k_ring, v_ring, out_ring, scale=None, stream=None, ctx=None):
+        """Attention of every live chunk (one launch), then every live chunk has
+        done one more step."""
+        S, L, H, D = _ring_args("Fifo.step", q_ring, k_ring, v_ring, out_ring)
+        if S != self.slots:
+            raise ValueError(f"chunkattn.Fifo.step: rings have {S} slots, queue {self.slots}")
+        scale = D ** -0.5 if scale is None else float(scale)
+        ctx = ctx or create(q_ring.device.index or 0)
+        rc = load_library().chunkattn_fifo_step(
+            ctx.handle, self.handle, _ptr(q_ring), _ptr(k_ring), _ptr(v_ring), _ptr(out_ring),
+            L, H, D, scale, _dtype_code(q_ring), _stream(q_ring, stream))
+        _check(rc, ctx.handle)
+        return out_ring
+
+
 def full(q, k, v, out=None, scale=None, stream=None, ctx=None):
     """Non-chunked attention of every query row over all K/V rows of its batch item.
 
@@ -338,4 +448,13 @@ def validate_window_step(q_ptr, k_ptr, v_ptr, cache_ptr, out_ptr, chunk_len, n_c
     lib = load_library()
     rc = lib.chunkattn_validate_window_step(q_ptr, k_ptr, v_ptr, cache_ptr, out_ptr, chunk_len,
                                             n_chunks, heads, head_dim, scale, dtype)
+    return rc, lib.chunkattn_last_error(None).decode()
+
+
+def validate_ring_step(q_ptr, k_ptr, v_ptr, out_ptr, slots, tail_slot, n_live, chunk_len, heads,
+                       head_dim, scale, dtype):
+    """(status, message) of the device-free argument checks of ring_step."""
+    lib = load_library()
+    rc = lib.chunkattn_validate_ring_step(q_ptr, k_ptr, v_ptr, out_ptr, slots, tail_slot, n_live,
+                                          chunk_len, heads, head_dim, scale, dtype)
     return rc, lib.chunkattn_last_error(None).decode()

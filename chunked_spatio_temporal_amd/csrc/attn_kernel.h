@@ -80,6 +80,19 @@ struct KernelArgs {
   int pred_shift;
   int row_stride;     // heads * head_dim (elements between consecutive tokens)
   float scale_log2;   // scale * log2(e)
+  // Ring of chunk slots (streaming queue): with ring_slots > 0, batch index b
+  // (processing order, 0 = the newest chunk) lives in slot
+  // (ring_tail - b) mod ring_slots of q, k, v and out, and reads its
+  // predecessor in place from the slot of b - 1.  0: batch b is entry b.
+  int ring_slots;
+  int ring_tail;
+
+  // Physical entry of batch index b (b > -ring_slots).
+  __host__ __device__ __forceinline__ int64_t entry(int b) const {
+    if (ring_slots == 0) return b;
+    const int p = ring_tail - b;
+    return p < 0 ? p + ring_slots : p;
+  }
 };
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -225,13 +238,14 @@ __device__ __forceinline__ void attn_item_sync(const KernelArgs& a, const Item& 
   const int n_tiles = (total + kBN - 1) / kBN;
   const int64_t rs = a.row_stride;
 
-  const T* qb = static_cast<const T*>(a.q) + it.b * a.q_bstride + (int64_t)it.h * D;
-  const T* kown = static_cast<const T*>(a.k) + it.b * a.kv_bstride + (int64_t)it.h * D;
-  const T* vown = static_cast<const T*>(a.v) + it.b * a.kv_bstride + (int64_t)it.h * D;
+  const int64_t e = a.entry(it.b);  // physical entry (slot) of this chunk
+  const T* qb = static_cast<const T*>(a.q) + e * a.q_bstride + (int64_t)it.h * D;
+  const T* kown = static_cast<const T*>(a.k) + e * a.kv_bstride + (int64_t)it.h * D;
+  const T* vown = static_cast<const T*>(a.v) + e * a.kv_bstride + (int64_t)it.h * D;
   const T* kpre = kown;
   const T* vpre = vown;
   if (pred > 0) {
-    const int64_t pi = (int64_t)(it.b - a.pred_shift) * a.p_bstride + (int64_t)it.h * D;
+    const int64_t pi = a.entry(it.b - a.pred_shift) * a.p_bstride + (int64_t)it.h * D;
     kpre = static_cast<const T*>(a.pk) + pi;
     vpre = static_cast<const T*>(a.pv) + pi;
   }
@@ -523,7 +537,7 @@ __device__ __forceinline__ void attn_item_sync(const KernelArgs& a, const Item& 
       for (int i = 0; i < 16; ++i) acc += oacc[db][i];
     if (__syncthreads_or(!__builtin_isfinite(acc))) {
       if (tid == 0)
-        static_cast<T*>(a.o)[it.b * a.o_bstride + (int64_t)it.q0 * rs + (int64_t)it.h * D] =
+        static_cast<T*>(a.o)[e * a.o_bstride + (int64_t)it.q0 * rs + (int64_t)it.h * D] =
             overflow_marker<T>();
       return;
     }
@@ -531,7 +545,7 @@ __device__ __forceinline__ void attn_item_sync(const KernelArgs& a, const Item& 
   const float l_tot = l_half + other_half(l_half);
   const float inv = 1.0f / l_tot;
   if (qvalid) {
-    T* ob = static_cast<T*>(a.o) + it.b * a.o_bstride + (int64_t)qrow * rs + (int64_t)it.h * D;
+    T* ob = static_cast<T*>(a.o) + e * a.o_bstride + (int64_t)qrow * rs + (int64_t)it.h * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -558,7 +572,7 @@ template <int D, typename T, int W>
 __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_recheck(KernelArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const Item it = decode(a.plan, slot_to_work(blockIdx.x, a.plan.n_items, a.plan.n_xcd));
-  const T first = static_cast<const T*>(a.o)[it.b * a.o_bstride + (int64_t)it.q0 * a.row_stride +
+  const T first = static_cast<const T*>(a.o)[a.entry(it.b) * a.o_bstride + (int64_t)it.q0 * a.row_stride +
                                               (int64_t)it.h * D];
   if (!__builtin_isnan((float)first)) return;
   attn_item_sync<D, T, W, false>(a, it, smem);

@@ -7,10 +7,12 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <new>
 #include <string>
 
 #include "attn_kernel.h"
 #include "chunkattn.h"
+#include "fifo.h"
 
 struct chunkattn_ctx {
   int device = 0;
@@ -101,6 +103,21 @@ int validate_queue(std::string* err, const void* q, const void* k, const void* v
   if (items > 2147483647.0L)
     return set_err(err, CHUNKATTN_EUNSUPPORTED, "too many work items for one launch");
   return CHUNKATTN_OK;
+}
+
+int validate_ring(std::string* err, const void* q, const void* k, const void* v,
+                  const void* out, int slots, int tail_slot, int n_live, int L, int heads,
+                  int head_dim, float scale, int dtype) {
+  if (slots < 1) return set_err(err, CHUNKATTN_EINVAL, "slots must be >= 1 (got %d)", slots);
+  if (n_live < 0 || n_live > slots)
+    return set_err(err, CHUNKATTN_EINVAL, "n_live must be in [0, slots] (got %d of %d)", n_live,
+                   slots);
+  if (tail_slot < 0 || tail_slot >= slots)
+    return set_err(err, CHUNKATTN_EINVAL, "tail_slot must be in [0, slots) (got %d of %d)",
+                   tail_slot, slots);
+  // the ring buffers hold `slots` chunks each
+  return validate_queue(err, q, k, v, nullptr, out, L, n_live == 0 ? 0 : slots, heads,
+                        head_dim, scale, dtype);
 }
 
 int validate_full(std::string* err, const void* q, const void* k, const void* v,
@@ -306,7 +323,7 @@ int chunkattn_queue_step(chunkattn_ctx* ctx, const void* q, const void* k, const
   }
   const int64_t per_chunk = (int64_t)chunk_len * heads * head_dim;
   const size_t es = elem_size(dtype);
-  KernelArgs a;
+  KernelArgs a{};  // zero: linear batch entries unless set below
   a.plan = chunkattn::make_plan(n_chunks, 1, heads, chunk_len, chunk_len, chunk_len,
                                 32 * ctx->waves, ctx->n_xcd);
   a.q = q;
@@ -343,7 +360,7 @@ int chunkattn_full(chunkattn_ctx* ctx, const void* q, const void* k, const void*
     ctx->err.clear();
     return CHUNKATTN_OK;
   }
-  KernelArgs a;
+  KernelArgs a{};  // zero: linear batch entries unless set below
   a.plan = chunkattn::make_plan(batch, batch, heads, lq, lkv, 0, 32 * ctx->waves, ctx->n_xcd);
   a.q = q;
   a.k = k;
@@ -383,7 +400,7 @@ int chunkattn_window_step(chunkattn_ctx* ctx, const void* q, const void* k, cons
   }
   const int64_t per_chunk = (int64_t)chunk_len * heads * head_dim;
   const size_t es = elem_size(dtype);
-  KernelArgs a;
+  KernelArgs a{};  // zero: linear batch entries unless set below
   a.plan = window_plan(chunk_len, n_chunks, heads, 32 * ctx->waves, ctx->n_xcd);
   a.q = q;
   a.k = k;
@@ -433,6 +450,131 @@ int chunkattn_window_plan_debug(int chunk_len, int n_chunks, int heads, int n_xc
     r[6] = it.own_rows;
   }
   return CHUNKATTN_OK;
+}
+
+int chunkattn_validate_ring_step(const void* q_ring, const void* k_ring, const void* v_ring,
+                                 const void* out_ring, int slots, int tail_slot, int n_live,
+                                 int chunk_len, int heads, int head_dim, float scale,
+                                 int dtype) {
+  g_thread_err.clear();
+  return validate_ring(&g_thread_err, q_ring, k_ring, v_ring, out_ring, slots, tail_slot, n_live,
+                       chunk_len, heads, head_dim, scale, dtype);
+}
+
+int chunkattn_ring_step(chunkattn_ctx* ctx, const void* q_ring, const void* k_ring,
+                        const void* v_ring, void* out_ring, int slots, int tail_slot,
+                        int n_live, int chunk_len, int heads, int head_dim, float scale,
+                        int dtype, void* hip_stream) {
+  if (!ctx) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "ctx must be non-NULL");
+  int rc = validate_ring(&ctx->err, q_ring, k_ring, v_ring, out_ring, slots, tail_slot, n_live,
+                         chunk_len, heads, head_dim, scale, dtype);
+  if (rc) return rc;
+  if (chunk_len == 0 || n_live == 0) {
+    ctx->err.clear();
+    return CHUNKATTN_OK;
+  }
+  const int64_t per_chunk = (int64_t)chunk_len * heads * head_dim;
+  KernelArgs a{};
+  a.plan = chunkattn::make_plan(n_live, 1, heads, chunk_len, chunk_len, chunk_len,
+                                32 * ctx->waves, ctx->n_xcd);
+  a.q = q_ring;
+  a.k = k_ring;
+  a.v = v_ring;
+  a.o = out_ring;
+  a.q_bstride = per_chunk;
+  a.o_bstride = per_chunk;
+  a.kv_bstride = per_chunk;
+  a.pk = k_ring;  // the predecessor is read in place from its slot
+  a.pv = v_ring;
+  a.p_bstride = per_chunk;
+  a.pred_shift = 1;
+  a.ring_slots = slots;
+  a.ring_tail = tail_slot;
+  a.row_stride = heads * head_dim;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return run(ctx, a, head_dim, dtype, hip_stream);
+}
+
+struct chunkattn_fifo {
+  chunkattn::Fifo q;
+};
+
+int chunkattn_fifo_create(chunkattn_fifo** out, int slots, int depth) {
+  g_thread_err.clear();
+  if (!out) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "out must be non-NULL");
+  *out = nullptr;
+  if (depth < 1 || slots < depth)
+    return set_err(&g_thread_err, CHUNKATTN_EINVAL,
+                   "need depth >= 1 and slots >= depth (got slots %d, depth %d)", slots, depth);
+  chunkattn_fifo* f = new (std::nothrow) chunkattn_fifo{chunkattn::Fifo(slots, depth)};
+  if (!f) return set_err(&g_thread_err, CHUNKATTN_ENOMEM, "cannot allocate the queue");
+  *out = f;
+  return CHUNKATTN_OK;
+}
+
+int chunkattn_fifo_destroy(chunkattn_fifo* f) {
+  delete f;
+  return CHUNKATTN_OK;
+}
+
+int chunkattn_fifo_push(chunkattn_fifo* f, int* slot) {
+  g_thread_err.clear();
+  if (!f || !slot) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "f and slot must be non-NULL");
+  if (f->q.full())
+    return set_err(&g_thread_err, CHUNKATTN_EINVAL, "queue full (%d chunks)", f->q.depth());
+  *slot = f->q.push();
+  return CHUNKATTN_OK;
+}
+
+int chunkattn_fifo_pop(chunkattn_fifo* f, int* slot) {
+  g_thread_err.clear();
+  if (!f || !slot) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "f and slot must be non-NULL");
+  if (!f->q.head_clean())
+    return set_err(&g_thread_err, CHUNKATTN_EINVAL,
+                   "the head chunk has not done all %d steps (or the queue is empty)",
+                   f->q.depth());
+  *slot = f->q.pop();
+  return CHUNKATTN_OK;
+}
+
+int chunkattn_fifo_live(const chunkattn_fifo* f, long long* ids, int* slots, int* steps_done,
+                        int cap, int* n_live) {
+  g_thread_err.clear();
+  if (!f || !n_live || cap < 0)
+    return set_err(&g_thread_err, CHUNKATTN_EINVAL, "bad fifo_live arguments");
+  *n_live = f->q.live();
+  for (int c = 0; c < f->q.live() && c < cap; ++c) {
+    int64_t id;
+    int s, d;
+    f->q.at(c, &id, &s, &d);
+    if (ids) ids[c] = id;
+    if (slots) slots[c] = s;
+    if (steps_done) steps_done[c] = d;
+  }
+  return CHUNKATTN_OK;
+}
+
+int chunkattn_fifo_advance(chunkattn_fifo* f) {
+  g_thread_err.clear();
+  if (!f) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "f must be non-NULL");
+  if (f->q.live() == 0) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "queue empty");
+  f->q.advance();
+  return CHUNKATTN_OK;
+}
+
+int chunkattn_fifo_step(chunkattn_ctx* ctx, chunkattn_fifo* f, const void* q_ring,
+                        const void* k_ring, const void* v_ring, void* out_ring, int chunk_len,
+                        int heads, int head_dim, float scale, int dtype, void* hip_stream) {
+  if (!f) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "f must be non-NULL");
+  if (f->q.live() == 0) {
+    std::string* sink = ctx ? &ctx->err : &g_thread_err;
+    return set_err(sink, CHUNKATTN_EINVAL, "queue empty: push a chunk first");
+  }
+  const int rc = chunkattn_ring_step(ctx, q_ring, k_ring, v_ring, out_ring, f->q.slots(),
+                                     f->q.tail_slot(), f->q.live(), chunk_len, heads, head_dim,
+                                     scale, dtype, hip_stream);
+  if (rc == CHUNKATTN_OK) f->q.advance();
+  return rc;
 }
 
 const char* chunkattn_status_string(int status) {

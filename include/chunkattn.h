@@ -138,6 +138,66 @@ int chunkattn_window_step(chunkattn_ctx *ctx, const void *q, const void *k, cons
                           int heads, int head_dim, float scale, int dtype, void *hip_stream);
 
 /*
+ * Streaming queue (DualParal write-up, section 二): new noisy chunks enter at
+ * the tail, clean chunks leave at the head, every step processes the whole
+ * queue tail first, and the video can grow without bound.  The chunks live in
+ * caller-owned ring buffers of `slots` chunk slots; nothing is copied when the
+ * queue advances.
+ *
+ * chunkattn_ring_step: one queue step over n_live chunks of a ring.  With the
+ * live chunks in processing order (c = 0 the tail, the newest), chunk c is in
+ * slot (tail_slot - c) mod slots; it attends over R_c = [its predecessor's
+ * K/V, read in place from the slot of chunk c-1 (c >= 1)] ++ [its own K/V],
+ * exactly as chunkattn_queue_step, and its output goes to the same slot of
+ * out_ring.  Other slots of out_ring are not written.
+ *
+ *   q_ring, k_ring, v_ring, out_ring  [slots][chunk_len][heads][head_dim],
+ *            device, 16-byte aligned; out_ring must not overlap an input.
+ *   slots >= 1; 0 <= tail_slot < slots; 0 <= n_live <= slots (0: no-op).
+ *   Other arguments as for chunkattn_queue_step.
+ */
+int chunkattn_ring_step(chunkattn_ctx *ctx, const void *q_ring, const void *k_ring,
+                        const void *v_ring, void *out_ring, int slots, int tail_slot,
+                        int n_live, int chunk_len, int heads, int head_dim, float scale,
+                        int dtype, void *hip_stream);
+
+/*
+ * Host-side queue bookkeeping for chunkattn_ring_step.  Chunk number g (in
+ * order of arrival, from 0) lives in slot g mod slots; a chunk spends exactly
+ * `depth` steps in the queue (one per noise level), so at most depth chunks
+ * are live and slots >= depth keeps them in distinct slots.  A queue object is
+ * used by one host thread at a time.  Failures return a status; the
+ * explanation is in chunkattn_last_error(NULL).
+ */
+typedef struct chunkattn_fifo chunkattn_fifo;
+
+/* New empty queue; needs depth >= 1 and slots >= depth. */
+int chunkattn_fifo_create(chunkattn_fifo **out, int slots, int depth);
+int chunkattn_fifo_destroy(chunkattn_fifo *f);
+/* A new chunk joins at the tail; *slot receives its slot, which the caller
+ * fills with the chunk's Q/K/V.  CHUNKATTN_EINVAL if depth chunks are live. */
+int chunkattn_fifo_push(chunkattn_fifo *f, int *slot);
+/* The head chunk leaves; *slot receives its slot (its last output is final).
+ * CHUNKATTN_EINVAL unless the head has done all depth steps. */
+int chunkattn_fifo_pop(chunkattn_fifo *f, int *slot);
+/* The live chunks in processing order (tail first): chunk numbers, slots and
+ * steps done, at most cap of each (any of the three arrays may be NULL);
+ * *n_live receives the count. */
+int chunkattn_fifo_live(const chunkattn_fifo *f, long long *ids, int *slots, int *steps_done,
+                        int cap, int *n_live);
+/* Every live chunk has done one more step, without a launch: for callers that
+ * run chunkattn_ring_step themselves (tail = slot of live chunk 0, n_live).
+ * CHUNKATTN_EINVAL if the queue is empty. */
+int chunkattn_fifo_advance(chunkattn_fifo *f);
+/* One diffusion step of the attention over every live chunk
+ * (chunkattn_ring_step with the queue's tail and count), after which every
+ * live chunk has done one more step.  CHUNKATTN_EINVAL if the queue is empty;
+ * on any failure the queue is unchanged. */
+int chunkattn_fifo_step(chunkattn_ctx *ctx, chunkattn_fifo *f, const void *q_ring,
+                        const void *k_ring, const void *v_ring, void *out_ring, int chunk_len,
+                        int heads, int head_dim, float scale, int dtype, void *hip_stream);
+
+/*
  * Non-chunked attention: every query row of batch item b attends over all lkv
  * rows of its K/V (the full-sequence attention the chunked form avoids, and
  * the per-chunk cross-attention to text tokens, which uses no cache).
@@ -169,6 +229,10 @@ int chunkattn_validate_window_step(const void *q, const void *k, const void *v,
                                    const void *kv_cache, const void *out, int chunk_len,
                                    int n_chunks, int heads, int head_dim, float scale,
                                    int dtype);
+int chunkattn_validate_ring_step(const void *q_ring, const void *k_ring, const void *v_ring,
+                                 const void *out_ring, int slots, int tail_slot, int n_live,
+                                 int chunk_len, int heads, int head_dim, float scale,
+                                 int dtype);
 
 /* Static description of a status code. */
 const char *chunkattn_status_string(int status);

@@ -261,3 +261,73 @@ def test_slot_to_work_is_a_bijection(n_items, xcd):
     got = items[:, 2] // bm                      # tile index == work index here
     np.testing.assert_array_equal(got, _slot_to_work_reference(n_items, xcd))
     assert sorted(got.tolist()) == list(range(n_items))
+
+
+# ------------------------------------------------------- streaming queue (host)
+
+from oracle import fifo as fifo_sim  # noqa: E402
+
+
+@pytest.mark.parametrize("total,slots,depth", [(1, 1, 1), (5, 3, 3), (11, 5, 4), (20, 8, 8),
+                                               (9, 12, 4), (3, 6, 4)])
+def test_fifo_bookkeeping_matches_the_queue_simulation(total, slots, depth):
+    """The C++ queue and the plain simulation of the page's FIFO agree on every
+    step: which slot a new chunk gets, the live chunks in processing order with
+    their slots and steps done, and which slot a clean chunk frees."""
+    f = ca.Fifo(slots, depth)
+    pushed_left = total
+    for pushed, live, popped in fifo_sim.run(total, slots, depth):
+        got_push = f.push() if pushed_left > 0 else -1
+        pushed_left -= got_push >= 0
+        assert got_push == pushed
+        assert f.live() == live
+        f.advance()
+        head = f.live()[-1]
+        got_pop = f.pop() if head[2] == depth else -1
+        assert got_pop == popped
+    assert f.live() == []
+
+
+def test_fifo_rejects_misuse():
+    with pytest.raises(ca.ChunkAttnError):
+        ca.Fifo(3, 4)                  # fewer slots than depth
+    with pytest.raises(ca.ChunkAttnError):
+        ca.Fifo(3, 0)
+    f = ca.Fifo(4, 2)
+    with pytest.raises(ca.ChunkAttnError):
+        f.advance()                    # empty
+    with pytest.raises(ca.ChunkAttnError):
+        f.pop()                        # empty
+    f.push()
+    f.push()
+    with pytest.raises(ca.ChunkAttnError):
+        f.push()                       # full
+    f.advance()
+    with pytest.raises(ca.ChunkAttnError):
+        f.pop()                        # head has done 1 of 2 steps
+    f.advance()
+    assert f.pop() == 0 and f.push() == 2
+
+
+def vr(**kw):
+    a = dict(q=P, k=2 * P, v=3 * P, out=4 * P, S=5, tail=3, n=4, L=16, H=2, D=128, scale=0.1,
+             dtype=ca.BF16)
+    a.update(kw)
+    return ca.validate_ring_step(a["q"], a["k"], a["v"], a["out"], a["S"], a["tail"], a["n"],
+                                 a["L"], a["H"], a["D"], a["scale"], a["dtype"])
+
+
+def test_validate_ring_step():
+    assert vr()[0] == ca.OK
+    assert vr(n=5)[0] == ca.OK
+    assert vr(n=0, q=None, k=None, v=None, out=None)[0] == ca.OK
+    for kw, code in [(dict(n=6), ca.EINVAL), (dict(tail=5), ca.EINVAL), (dict(tail=-1), ca.EINVAL),
+                     (dict(S=0), ca.EINVAL), (dict(D=80), ca.EUNSUPPORTED),
+                     (dict(out=P + 16), ca.EINVAL), (dict(q=None), ca.EINVAL)]:
+        rc, msg = vr(**kw)
+        assert rc == code, (kw, msg)
+
+
+def test_ring_step_without_context_is_rejected():
+    assert lib.chunkattn_ring_step(None, P, 2 * P, 3 * P, 4 * P, 5, 0, 2, 16, 2, 128,
+                                   ctypes.c_float(0.1), 0, None) == ca.EINVAL

@@ -74,7 +74,15 @@ def main():
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
     t0 = time.time()
-    if w.kind in ("queue", "window"):
+    fifo = None
+    if w.kind == "stream":
+        # ring of n+1 slots; fill the queue until its head is clean (steady state)
+        S = w.n + 1
+        q, k, v = synth.queue_inputs(S, w.L, w.H, w.D, w.seed, device=dev, dtype=dt,
+                                     k_rho=w.k_rho, v_rho=w.v_rho)
+        cache = None
+        out = torch.empty_like(q)
+    elif w.kind in ("queue", "window"):
         q, k, v = synth.queue_inputs(w.n, w.L, w.H, w.D, w.seed, device=dev, dtype=dt,
                                      k_rho=w.k_rho, v_rho=w.v_rho)
         cache = synth.build_cache(k, v)
@@ -100,8 +108,20 @@ def main():
     flags = {0: 0, 128: ca.FLAG_BLOCK128, 256: ca.FLAG_BLOCK256}[args.block_rows]
     ctx = ca.create(0, flags)
 
+    if w.kind == "stream":
+        fifo = ca.Fifo(w.n + 1, w.n)
+        for _ in range(w.n):
+            fifo.push()
+            fifo.step(q, k, v, out, scale=w.scale, stream=stream, ctx=ctx)
+        fifo.pop()
+
     def dominant():
-        if w.kind == "queue":
+        if w.kind == "stream":
+            # steady state: a chunk enters, all n live chunks are processed, the head leaves
+            fifo.push()
+            fifo.step(q, k, v, out, scale=w.scale, stream=stream, ctx=ctx)
+            fifo.pop()
+        elif w.kind == "queue":
             ca.queue_step(q, k, v, cache, out=out, scale=w.scale, stream=stream, ctx=ctx)
         elif w.kind == "window":
             ca.window_step(q, k, v, cache, out=out, scale=w.scale, stream=stream, ctx=ctx)
@@ -198,7 +218,10 @@ def main():
             "lkv": w.lkv if w.kind == "full" else None,
             "window": ("queries of chunks c and c+1; keys of chunks c-1 (cached), c, c+1"
                        if w.kind == "window" else None),
-            "kv_cache": "separate buffer" if cache is not None else None,
+            "kv_cache": ("separate buffer" if cache is not None else
+                         "predecessor read in place from its ring slot"
+                         if w.kind == "stream" else None),
+            "ring_slots": w.n + 1 if w.kind == "stream" else None,
             "text_tokens": w.n_text or None,
             "block_rows": ctx.block_rows,
             "flops_per_step": flops_step,
@@ -210,7 +233,14 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        record["cpu_baseline"] = cpu_baseline(w, q, k, v, cache, args.cpu_seconds)
+        if w.kind == "stream":
+            # the live chunks in processing order: chunk 0 (the tail) and its successor
+            live = [s for _, s, _ in fifo.live()]
+            lin = lambda t: t[live].contiguous()
+            record["cpu_baseline"] = cpu_baseline(w, lin(q), lin(k), lin(v), None,
+                                                  args.cpu_seconds)
+        else:
+            record["cpu_baseline"] = cpu_baseline(w, q, k, v, cache, args.cpu_seconds)
 
     print(json.dumps(record), flush=True)
 
@@ -228,7 +258,7 @@ def cpu_baseline(w, q, k, v, cache, seconds):
     import oracle
 
     rng = np.random.default_rng(1234)
-    if w.kind == "queue":
+    if w.kind in ("queue", "stream"):
         chunks = [0, 1] if w.n > 1 else [0]
         lo = max(chunks[-1] - 1, 0)
         sub = lambda t: t[lo:chunks[-1] + 1].cpu()

@@ -14,7 +14,7 @@ from dataclasses import dataclass, field
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "queue", "window" or "full"
+    kind: str                 # "queue", "window", "stream" or "full"
     n: int                    # chunks (queue) or batch (full)
     L: int                    # tokens per chunk (queue) or Lq (full)
     H: int
@@ -34,7 +34,7 @@ class Workload:
 
     def self_flops(self) -> float:
         """Exact FLOPs of the self-attention call."""
-        if self.kind == "queue":
+        if self.kind in ("queue", "stream"):
             if self.n == 0:
                 return 0.0
             kv_rows = self.L * self.L + (self.n - 1) * self.L * 2 * self.L
@@ -81,6 +81,11 @@ WORKLOADS = {
                        k_rho=0.9, seed=5, grid=(4, 30, 52),
                        note="the 40-head queue in the three-chunk window form: window c's "
                             "queries are chunks c and c+1, its keys chunks c-1 (cached), c, c+1"),
+    "stream14b": Workload("stream14b", "stream", n=8, L=6240, H=40, D=128, dtype="bf16",
+                          k_rho=0.9, seed=6, grid=(4, 30, 52),
+                          note="the 40-head queue as a stream in steady state: 8 live chunks "
+                               "in a ring of 9 slots; each step a chunk enters, all 8 are "
+                               "processed, the clean head leaves"),
 }
 
 # The timed workload: the 40-head, 480p-latent queue step.

@@ -552,3 +552,63 @@ def test_fifo_rejects_misuse():
     assert f.pop() == 0
     with pytest.raises(ValueError):
         fifo_sim.Fifo(3, 4)
+
+
+# --------------------------------------------------------------------------
+# coordinated noise initialization (DualParal write-up, section 三)
+
+from oracle import noise as noise_sim  # noqa: E402
+
+
+def test_noise_select_closed_forms():
+    # keys order the candidates: pool 6, tail chunk used [4, 0, 5, 2] (last 2: 5, 2)
+    keys = np.array([50, 10, 40, 30, 20, 60], np.uint32)
+    idx = noise_sim.select(6, keys, 3, prev_idx=[4, 0, 5, 2], n_excl=2)
+    # candidates {0, 1, 3, 4} by key: 1 (10), 4 (20), 3 (30), 0 (50)
+    assert idx.tolist() == [1, 4, 3]
+    # equal keys fall back to the pool index
+    assert noise_sim.select(4, [7, 7, 7, 7], 4).tolist() == [0, 1, 2, 3]
+    # the first chunk has nothing to avoid
+    assert noise_sim.select(6, keys, 6).tolist() == [1, 4, 3, 2, 0, 5]
+    # pool exactly F + E: the new chunk takes every frame the neighbour's tail did not use
+    idx = noise_sim.select(6, keys, 4, prev_idx=[0, 1, 2, 3], n_excl=2)
+    assert sorted(idx.tolist()) == [0, 1, 4, 5]
+
+
+def test_noise_select_properties_over_a_long_video():
+    """Chunk after chunk: frames are distinct within a chunk, never reuse what
+    the neighbour's last E frames used, every pool frame keeps being used (the
+    whole noise space), and the copies are exact."""
+    P, F, E = 12, 8, 4
+    rng = np.random.default_rng(5)
+    pool = rng.standard_normal((P, 3, 5)).astype(np.float32)
+    prev, used = None, set()
+    for _ in range(40):
+        keys = rng.integers(0, 2 ** 32, P, dtype=np.uint64).astype(np.uint32)
+        idx = noise_sim.select(P, keys, F, prev, E)
+        assert len(set(idx.tolist())) == F and ((0 <= idx) & (idx < P)).all()
+        if prev is not None:
+            assert not set(idx.tolist()) & set(prev[F - E:].tolist())
+        chunk = noise_sim.init_chunk(pool, idx)
+        assert np.array_equal(chunk, pool[idx])
+        used |= set(idx.tolist())
+        prev = idx
+    assert used == set(range(P))
+
+
+def test_noise_select_is_a_uniform_shuffle():
+    """With uniform keys every candidate is equally likely at every position."""
+    P, F = 5, 5
+    rng = np.random.default_rng(11)
+    counts = np.zeros((F, P))
+    trials = 4000
+    for _ in range(trials):
+        keys = rng.integers(0, 2 ** 32, P, dtype=np.uint64).astype(np.uint32)
+        for f, p in enumerate(noise_sim.select(P, keys, F)):
+            counts[f, p] += 1
+    assert np.abs(counts / trials - 1 / P).max() < 0.035
+
+
+def test_noise_select_rejects_too_small_pool():
+    with pytest.raises(ValueError):
+        noise_sim.select(5, np.zeros(5, np.uint32), 4, prev_idx=[0, 1, 2, 3], n_excl=2)

@@ -97,6 +97,10 @@ def load_library():
     lib.chunkattn_fifo_advance.argtypes = [vp]
     lib.chunkattn_fifo_step.restype = i32
     lib.chunkattn_fifo_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, i32, vp]
+    lib.chunkattn_noise_init.restype = i32
+    lib.chunkattn_noise_init.argtypes = [vp, vp, i32, i64, vp, vp, i32, i32, i32, vp, vp, vp]
+    lib.chunkattn_validate_noise_init.restype = i32
+    lib.chunkattn_validate_noise_init.argtypes = [vp, i32, i64, vp, vp, i32, i32, i32, vp, vp]
     lib.chunkattn_ctx_xcd_count.restype = i32
     lib.chunkattn_ctx_xcd_count.argtypes = [vp]
     _lib = lib
@@ -345,6 +349,47 @@ class Fifo:
             L, H, D, scale, _dtype_code(q_ring), _stream(q_ring, stream))
         _check(rc, ctx.handle)
         return out_ring
+
+
+def noise_init(pool, keys, n_frames, prev_idx=None, n_excl=0, out=None, idx_out=None,
+               stream=None, ctx=None):
+    """A new chunk's noise: n_frames frames of `pool` [P, ...] (any dtype), the
+    candidates not used by the last n_excl entries of prev_idx, ranked by
+    (keys, index); keys is an int32/uint32 tensor of P values (bit patterns
+    compared as unsigned).  Returns (out [n_frames, ...], idx_out int32)."""
+    import torch
+    P = pool.shape[0]
+    _require(pool, "pool", pool.device)
+    _require(keys, "keys", pool.device)
+    if keys.shape != (P,) or keys.element_size() != 4:
+        raise ValueError("chunkattn.noise_init: keys must be P 32-bit values")
+    frame_bytes = pool[0].numel() * pool.element_size() if P else 0
+    n_prev = 0
+    if prev_idx is not None:
+        _require(prev_idx, "prev_idx", pool.device)
+        if prev_idx.dtype != torch.int32 or prev_idx.dim() != 1:
+            raise ValueError("chunkattn.noise_init: prev_idx must be 1-D int32")
+        n_prev = prev_idx.numel()
+    if out is None:
+        out = torch.empty((n_frames,) + tuple(pool.shape[1:]), dtype=pool.dtype,
+                          device=pool.device)
+    if idx_out is None:
+        idx_out = torch.empty(n_frames, dtype=torch.int32, device=pool.device)
+    ctx = ctx or create(pool.device.index or 0)
+    rc = load_library().chunkattn_noise_init(
+        ctx.handle, _ptr(pool), P, frame_bytes, _ptr(keys), _ptr(prev_idx), n_prev, int(n_excl),
+        int(n_frames), _ptr(out), _ptr(idx_out), _stream(pool, stream))
+    _check(rc, ctx.handle)
+    return out, idx_out
+
+
+def validate_noise_init(pool_ptr, pool_frames, frame_bytes, keys_ptr, prev_ptr, n_prev, n_excl,
+                        n_frames, out_ptr, idx_ptr):
+    """(status, message) of the device-free argument checks of noise_init."""
+    lib = load_library()
+    rc = lib.chunkattn_validate_noise_init(pool_ptr, pool_frames, frame_bytes, keys_ptr,
+                                           prev_ptr, n_prev, n_excl, n_frames, out_ptr, idx_ptr)
+    return rc, lib.chunkattn_last_error(None).decode()
 
 
 def full(q, k, v, out=None, scale=None, stream=None, ctx=None):

@@ -13,6 +13,7 @@
 #include "attn_kernel.h"
 #include "chunkattn.h"
 #include "fifo.h"
+#include "noise.h"
 
 struct chunkattn_ctx {
   int device = 0;
@@ -575,6 +576,78 @@ int chunkattn_fifo_step(chunkattn_ctx* ctx, chunkattn_fifo* f, const void* q_rin
                                      scale, dtype, hip_stream);
   if (rc == CHUNKATTN_OK) f->q.advance();
   return rc;
+}
+
+int chunkattn_validate_noise_init(const void* pool, int pool_frames, long long frame_bytes,
+                                  const void* keys, const void* prev_idx, int n_prev,
+                                  int n_excl, int n_frames, const void* out,
+                                  const void* idx_out) {
+  g_thread_err.clear();
+  std::string* err = &g_thread_err;
+  if (pool_frames < 1 || pool_frames > chunkattn::kMaxNoisePool)
+    return set_err(err, CHUNKATTN_EINVAL, "pool_frames must be in [1, %d] (got %d)",
+                   chunkattn::kMaxNoisePool, pool_frames);
+  if (n_frames < 1) return set_err(err, CHUNKATTN_EINVAL, "n_frames must be >= 1");
+  if (n_prev < 0 || n_excl < 0 || n_excl > n_prev)
+    return set_err(err, CHUNKATTN_EINVAL, "need 0 <= n_excl <= n_prev (got %d, %d)", n_excl,
+                   n_prev);
+  if (n_prev > 0 && !prev_idx)
+    return set_err(err, CHUNKATTN_EINVAL, "prev_idx must be non-NULL when n_prev > 0");
+  if ((long long)pool_frames - n_excl < n_frames)
+    return set_err(err, CHUNKATTN_EINVAL,
+                   "pool of %d frames minus %d excluded cannot give %d frames", pool_frames,
+                   n_excl, n_frames);
+  if (frame_bytes < 16 || frame_bytes % 16)
+    return set_err(err, CHUNKATTN_EINVAL, "frame_bytes must be a positive multiple of 16");
+  if ((long double)frame_bytes * pool_frames > 4.0e18L || frame_bytes / 16 / 256 >= (1LL << 31))
+    return set_err(err, CHUNKATTN_EINVAL, "pool or frame size too large");
+  if (!pool || !keys || !out || !idx_out)
+    return set_err(err, CHUNKATTN_EINVAL, "pool, keys, out and idx_out must be non-NULL");
+  if (!aligned16(pool) || !aligned16(out) || (reinterpret_cast<uintptr_t>(keys) & 3) ||
+      (reinterpret_cast<uintptr_t>(idx_out) & 3) ||
+      (prev_idx && (reinterpret_cast<uintptr_t>(prev_idx) & 3)))
+    return set_err(err, CHUNKATTN_EINVAL,
+                   "pool and out must be 16-byte aligned, keys and index arrays 4-byte aligned");
+  const size_t pool_b = (size_t)pool_frames * frame_bytes, out_b = (size_t)n_frames * frame_bytes;
+  if (overlaps(out, out_b, pool, pool_b) || overlaps(idx_out, 4 * (size_t)n_frames, out, out_b) ||
+      overlaps(idx_out, 4 * (size_t)n_frames, keys, 4 * (size_t)pool_frames) ||
+      (prev_idx && overlaps(idx_out, 4 * (size_t)n_frames, prev_idx, 4 * (size_t)n_prev)))
+    return set_err(err, CHUNKATTN_EINVAL, "outputs overlap an input");
+  return CHUNKATTN_OK;
+}
+
+int chunkattn_noise_init(chunkattn_ctx* ctx, const void* pool, int pool_frames,
+                         long long frame_bytes, const void* keys, const void* prev_idx,
+                         int n_prev, int n_excl, int n_frames, void* out, void* idx_out,
+                         void* hip_stream) {
+  if (!ctx) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "ctx must be non-NULL");
+  int rc = chunkattn_validate_noise_init(pool, pool_frames, frame_bytes, keys, prev_idx, n_prev,
+                                         n_excl, n_frames, out, idx_out);
+  if (rc) {
+    ctx->err = g_thread_err;
+    return rc;
+  }
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return set_err(&ctx->err, CHUNKATTN_EDEVICE, "cannot make device current");
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  hipLaunchKernelGGL(chunkattn::noise_select, dim3(1), dim3(256), 0, st,
+                     static_cast<const uint32_t*>(keys), pool_frames,
+                     static_cast<const int*>(prev_idx), n_prev, n_excl, n_frames,
+                     static_cast<int*>(idx_out));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return set_err(&ctx->err, CHUNKATTN_ELAUNCH, "noise_select launch failed: %s",
+                   hipGetErrorString(e));
+  const int64_t vecs = frame_bytes / 16;
+  hipLaunchKernelGGL(chunkattn::noise_gather, dim3((unsigned)((vecs + 255) / 256), n_frames),
+                     dim3(256), 0, st, static_cast<const uint4*>(pool), vecs,
+                     static_cast<const int*>(idx_out), static_cast<uint4*>(out));
+  e = hipGetLastError();
+  if (e != hipSuccess)
+    return set_err(&ctx->err, CHUNKATTN_ELAUNCH, "noise_gather launch failed: %s",
+                   hipGetErrorString(e));
+  ctx->err.clear();
+  return CHUNKATTN_OK;
 }
 
 const char* chunkattn_status_string(int status) {

@@ -198,6 +198,38 @@ int chunkattn_fifo_step(chunkattn_ctx *ctx, chunkattn_fifo *f, const void *q_rin
                         int heads, int head_dim, float scale, int dtype, void *hip_stream);
 
 /*
+ * Coordinated noise initialization of a new chunk (DualParal write-up,
+ * section 三, second improvement): the new chunk's n_frames noise frames come
+ * from a shared pool of pool_frames frames, leaving out the frames used by the
+ * last n_excl latent frames of the tail chunk (its temporal neighbour, NumC/2
+ * in the write-up), in a random order given by the caller's keys.
+ *
+ *   pool      [pool_frames][frame_bytes] device memory, 16-byte aligned;
+ *             frame_bytes a positive multiple of 16 (any element type: frames
+ *             are copied bit for bit).  1 <= pool_frames <= 4096.
+ *   keys      pool_frames uint32 on the device: the draw.  The candidates
+ *             (pool frames not excluded) in ascending (key, pool index) order
+ *             give the new frames: frame f is the candidate of rank f.
+ *   prev_idx  the tail chunk's pool indices in frame order (n_prev ints on the
+ *             device; NULL with n_prev = 0 for the first chunk); its last
+ *             n_excl entries are excluded (0 <= n_excl <= n_prev; values
+ *             outside [0, pool_frames) exclude nothing).
+ *   out       [n_frames][frame_bytes] device, 16-byte aligned: the new noise.
+ *   idx_out   n_frames ints on the device: the pool index of each new frame
+ *             (the next call's prev_idx).
+ *   Requires pool_frames - n_excl >= n_frames.  No output may overlap an
+ *   input.  Two launches on hip_stream.
+ */
+int chunkattn_noise_init(chunkattn_ctx *ctx, const void *pool, int pool_frames,
+                         long long frame_bytes, const void *keys, const void *prev_idx,
+                         int n_prev, int n_excl, int n_frames, void *out, void *idx_out,
+                         void *hip_stream);
+int chunkattn_validate_noise_init(const void *pool, int pool_frames, long long frame_bytes,
+                                  const void *keys, const void *prev_idx, int n_prev,
+                                  int n_excl, int n_frames, const void *out,
+                                  const void *idx_out);
+
+/*
  * Non-chunked attention: every query row of batch item b attends over all lkv
  * rows of its K/V (the full-sequence attention the chunked form avoids, and
  * the per-chunk cross-attention to text tokens, which uses no cache).

@@ -331,3 +331,24 @@ def test_validate_ring_step():
 def test_ring_step_without_context_is_rejected():
     assert lib.chunkattn_ring_step(None, P, 2 * P, 3 * P, 4 * P, 5, 0, 2, 16, 2, 128,
                                    ctypes.c_float(0.1), 0, None) == ca.EINVAL
+
+
+# ------------------------------------------------------ noise initialization
+
+def vn(**kw):
+    a = dict(pool=P, PF=12, fb=4096, keys=2 * P, prev=3 * P, n_prev=8, n_excl=4, F=8,
+             out=4 * P, idx=5 * P)
+    a.update(kw)
+    return ca.validate_noise_init(a["pool"], a["PF"], a["fb"], a["keys"], a["prev"], a["n_prev"],
+                                  a["n_excl"], a["F"], a["out"], a["idx"])
+
+
+def test_validate_noise_init():
+    assert vn()[0] == ca.OK
+    assert vn(prev=None, n_prev=0, n_excl=0)[0] == ca.OK          # first chunk
+    for kw in [dict(PF=0), dict(PF=4097), dict(F=0), dict(n_excl=9), dict(n_excl=-1),
+               dict(prev=None), dict(F=9),                        # 12 - 4 < 9
+               dict(fb=24), dict(fb=0), dict(pool=P + 8), dict(keys=2 * P + 2),
+               dict(out=P + 4096), dict(idx=4 * P + 16)]:
+        rc, msg = vn(**kw)
+        assert rc == ca.EINVAL, (kw, msg)

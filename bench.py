@@ -41,7 +41,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=None, help="workload name (default: the 40-head queue)")
+    ap.add_argument("--workload", default=None,
+                    help="workload name (default: the 40-head queue); also the noise-init "
+                         "workloads noise480p, noise480p_video")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -67,6 +69,9 @@ def main():
     from chunked_spatio_temporal_amd import configs, synth
 
     name = args.workload or configs.BENCH_WORKLOAD
+    if name in configs.NOISE_WORKLOADS:
+        bench_noise(args, configs.NOISE_WORKLOADS[name])
+        return
     w = configs.WORKLOADS[name]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -242,6 +247,88 @@ def main():
         else:
             record["cpu_baseline"] = cpu_baseline(w, q, k, v, cache, args.cpu_seconds)
 
+    print(json.dumps(record), flush=True)
+
+
+def bench_noise(args, w):
+    """Coordinated noise initialization, chained chunk after chunk (each init
+    avoids the frames the previous chunk's last `excl` frames used)."""
+    import numpy as np
+    import torch
+
+    from chunked_spatio_temporal_amd import chunkattn as ca
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    ca.load_library()
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    pool = torch.randn((w.pool_frames,) + w.frame_shape, generator=g, device=dev).to(dt)
+    n_keys = args.warmup + args.steps
+    keys = torch.randint(-2 ** 31, 2 ** 31 - 1, (n_keys, w.pool_frames), generator=g,
+                         device=dev, dtype=torch.int32)
+    outs = [torch.empty((w.frames,) + w.frame_shape, dtype=dt, device=dev) for _ in range(2)]
+    idxs = [torch.empty(w.frames, dtype=torch.int32, device=dev) for _ in range(2)]
+    stream = torch.cuda.current_stream(dev)
+    ctx = ca.create(0)
+    state = {"prev": None}
+
+    def init(i):
+        out, idx = outs[i % 2], idxs[i % 2]
+        prev = state["prev"]
+        ca.noise_init(pool, keys[i], w.frames, prev, w.excl if prev is not None else 0,
+                      out=out, idx_out=idx, stream=stream, ctx=ctx)
+        state["prev"] = idx
+
+    for i in range(args.warmup):
+        init(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for j in range(args.steps):
+        ev[j][0].record(stream)
+        init(args.warmup + j)
+        ev[j][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    launch = np.array([a.elapsed_time(b) for a, b in ev])
+    nbytes = w.bytes_per_init(pool.element_size())
+    gbs = nbytes / (launch.mean() * 1e-3) / 1e9
+    record = {
+        "metric": "coordinated noise init: GB/s (pool frames read + chunk written)",
+        "value": round(nbytes / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "pool_frames": w.pool_frames, "frames": w.frames,
+                   "excl": w.excl, "frame_shape": list(w.frame_shape),
+                   "bytes_per_step": nbytes},
+        "inits_per_s": round(1e3 / ms, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None,
+                     "kernel": "noise_select + noise_gather",
+                     "launch_ms_avg": round(float(launch.mean()), 5)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import noise as noise_sim
+        pool_h = pool.cpu().numpy() if dt == torch.float32 else pool.float().cpu().numpy()
+        keys_h = keys.cpu().numpy().view(np.uint32)
+        t0 = time.perf_counter()
+        count, prev = 0, None
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            idx = noise_sim.select(w.pool_frames, keys_h[count % n_keys], w.frames, prev,
+                                   w.excl if prev is not None else 0)
+            noise_sim.init_chunk(pool_h, idx)
+            prev, count = idx, count + 1
+        dt_cpu = time.perf_counter() - t0
+        record["cpu_baseline"] = {"value": round(count * nbytes / dt_cpu / 1e9, 3), "unit": "GB/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": f"{count} chained chunk inits in {dt_cpu:.1f} s"}
     print(json.dumps(record), flush=True)
 
 

@@ -90,3 +90,39 @@ WORKLOADS = {
 
 # The timed workload: the 40-head, 480p-latent queue step.
 BENCH_WORKLOAD = "wan14b"
+
+
+@dataclass(frozen=True)
+class NoiseWorkload:
+    """Coordinated noise initialization of one new chunk: `frames` latent
+    frames from a pool of `pool_frames`, avoiding the `excl` frames used by
+    the tail chunk's last latent frames."""
+    name: str
+    pool_frames: int
+    frames: int
+    excl: int
+    frame_shape: tuple        # (channels, height, width) of one latent frame
+    dtype: str
+    seed: int = 0
+    note: str = ""
+
+    def bytes_per_init(self, elem_bytes: int) -> int:
+        """Frames read from the pool plus frames written (the selection itself
+        moves a few KB)."""
+        n = 1
+        for x in self.frame_shape:
+            n *= x
+        return 2 * self.frames * n * elem_bytes
+
+
+NOISE_WORKLOADS = {
+    # 4 latent frames per chunk (the 480p queue's chunk: 4 frames of 30x52
+    # patches = 60x104 latents, 16 channels), pool of 2 chunks, NumC/2 = 2
+    "noise480p": NoiseWorkload("noise480p", pool_frames=8, frames=4, excl=2,
+                               frame_shape=(16, 60, 104), dtype="f32", seed=7,
+                               note="one chunk's noise for the 480p queue"),
+    # a whole 81-frame video's latents (21 frames) from a pool of 42
+    "noise480p_video": NoiseWorkload("noise480p_video", pool_frames=42, frames=21, excl=10,
+                                     frame_shape=(16, 60, 104), dtype="f32", seed=8,
+                                     note="21 latent frames from a pool of 42"),
+}

@@ -27,7 +27,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # device code of the attention kernels (the work plan and the kernel bodies);
 # the host code around them does not change what the counters measure
 KERNEL_SOURCES = [os.path.join(ROOT, "chunked_spatio_temporal_amd", "csrc", f)
-                  for f in ("attn_kernel.h", "plan.h")]
+                  for f in ("attn_kernel.h", "attn_pingpong.h", "plan.h")]
 
 
 def kernel_hash() -> str:
@@ -179,7 +179,8 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
         "traffic": None,
-        "kernel": f"chunk_attn_fwd<{w.D},{w.dtype},{ctx.block_rows // 32}>",
+        "kernel": (f"chunk_attn_fwd_pingpong<{w.D},{w.dtype}>" if ctx.block_rows == 256
+                   else f"chunk_attn_fwd<{w.D},{w.dtype},{ctx.block_rows // 32}>"),
         "launch_ms_avg": round(dom_avg_ms, 4),
         "launch_ms_min": round(float(launch_ms.min()), 4),
         "launch_ms_p90": round(float(np.percentile(launch_ms, 90)), 4),

@@ -171,6 +171,53 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds_chunk) {
 #endif
 }
 
+// The same load written as inline assembly.  After the builtin the compiler
+// makes every later LDS read wait for the load (it cannot tell the target
+// apart from what is read); it does not count these, so a kernel that uses
+// them waits itself (wait_vmem, wait_vmem_le) before it reads the tile.  The
+// block saves and restores M0, inserts the five wait states an M0 write (or a
+// base SGPR written by a vector instruction just before) needs ahead of an
+// LDS DMA, and clobbers memory so that no memory access moves across it.
+// Device pass only.
+__device__ __forceinline__ void load_lds16_async(const void* g, void* lds_chunk) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t m0 = (uint32_t)(uintptr_t)(CA_LDS void*)lds_chunk;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 4\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(m0)
+      : "memory");
+#endif
+}
+// With a wave-uniform base address (SGPRs) plus a per-lane 32-bit byte offset.
+__device__ __forceinline__ void load_lds16_async(const void* sbase, uint32_t voff,
+                                                 void* lds_chunk) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t m0 = (uint32_t)(uintptr_t)(CA_LDS void*)lds_chunk;
+  // The base is wave-uniform; make that explicit so it lives in SGPRs.  The
+  // builtin works on int: both halves are zero-extended back explicitly.
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 4\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sb), "s"(m0)
+      : "memory");
+#endif
+}
+
 // The value held by lane (l ^ 32): the other half of the wave, which holds the
 // other 32 keys of the same query row.  (ds_bpermute; the compiler used here
 // folds the two results of a same-operand v_permlane32_swap into one, which
@@ -180,6 +227,13 @@ __device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32);
 // s_waitcnt vmcnt(0): every global load of this wave (including the ones that
 // write LDS directly) has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): at most N of this wave's global loads are still in
+// flight.  A wave's loads complete in the order they were issued.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // Workgroup barrier that leaves in-flight global->LDS loads alone (unlike
 // __syncthreads, whose release fence waits for every outstanding global load).

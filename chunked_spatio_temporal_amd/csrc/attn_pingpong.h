@@ -1,0 +1,418 @@
+// gfx950 chunk-attention forward kernel, ping-pong schedule (256-row work
+// items, 8 waves of 32 query rows, two waves per SIMD).
+//
+// A SIMD issues matrix instructions from one wave while it issues vector-ALU
+// instructions from another, but inside one wave the in-order issue lets a
+// softmax dependency chain hold up the next MFMA.  So the two waves that share
+// a SIMD take turns: in every phase one of them does only matrix work (P.V of
+// the previous key tile and S = K.Q^T of the current one) and the other only
+// the softmax of the tile whose scores it just computed.  Waves 0-3 (group A)
+// and waves 4-7 (group B) sit on SIMDs 0-3 once each, so group A runs matrix
+// phases while group B runs softmax phases and the other way round; one
+// workgroup barrier ends every phase.
+//
+//   phase:     0      1      2      3      4   ...  2n     2n+1
+//   group A:  S(0)   sm(0)  PV(0)  sm(1)  PV(1) ... PV(n-1)  -
+//                           S(1)          S(2)
+//   group B:   -     S(0)   sm(0)  PV(0)  sm(1) ...  sm(n-1) PV(n-1)
+//                                  S(1)
+//
+// The wave in its matrix phase runs at the higher wave priority (s_setprio):
+// the two waves of a SIMD compete for instruction issue, and without it the
+// older wave's softmax slows the younger wave's matrix phase by a fifth.
+//
+// Softmax: fixed reference maximum per row (the maximum of the row's first
+// key tile), as in attn_kernel.h; a work item whose l or O overflows writes the
+// overflow marker and is redone by chunk_attn_recheck.  The denominator l is
+// summed by the matrix core (see lacc), so a score pair costs the softmax wave
+// two FMAs, two exponentials and one pack.
+//
+// The K/V tiles go global -> LDS by LDS DMA written as inline asm
+// (load_lds16_async): each wave waits for its own loads with vmcnt.
+//
+// LDS: rings of four K slots and four V slots (tile t in slot t mod 4).  The
+// loads of "group" g = {K(g), V(g-1)} (the tiles the matrix phase of tile g
+// reads for the first time) start in the softmax phase of tile g-3, three
+// phases or more before any wave reads them; each wave waits for its own
+// loads of group t+1 at the end of its matrix phase of tile t, and the
+// barrier that ends global phase 2t+1 publishes them.  A slot is reloaded
+// only after both groups have finished reading it (K(g) replaces K(g-4),
+// V(g-1) replaces V(g-5)).  Both groups run the same code: group B starts one
+// phase later (an extra barrier first) and group A ends with one.
+#pragma once
+
+#include <type_traits>
+
+#include "attn_kernel.h"
+
+namespace chunkattn {
+
+// Eight 64-row tiles: K slots 0..3, then V slots 0..3.
+template <int D>
+constexpr uint32_t kPingPongLdsBytes = 8 * Geo<D>::kTileBytes;
+
+// Empty asm statements that "modify" a value: they are ordered with the
+// workgroup barrier (both have side effects), so a value pinned on both sides
+// of a barrier is computed before it and only used after it.  The optimiser
+// would otherwise move the arithmetic of a phase across the barrier into the
+// other phase.
+__device__ __forceinline__ void pin(f32x16_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(uint32_t (&p)[8]) {
+  asm volatile("" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]));
+  asm volatile("" : "+v"(p[4]), "+v"(p[5]), "+v"(p[6]), "+v"(p[7]));
+}
+__device__ __forceinline__ void pin(float (&l)[4]) {
+  asm volatile("" : "+v"(l[0]), "+v"(l[1]), "+v"(l[2]), "+v"(l[3]));
+}
+
+template <int D, typename T>
+__device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const Item& it,
+                                                   unsigned char* smem) {
+  using G = Geo<D>;
+  constexpr int W = 8;
+  constexpr int kCpw = G::kChunks / W;  // 1 KB load chunks per wave per matrix
+  static_assert(kCpw >= 1 && kCpw * W == G::kChunks, "tile split across waves");
+  constexpr int kKs = D / 16;
+  constexpr int kDb = D / 32;
+  constexpr int kStepsQK = 2 * kKs;              // 2 key blocks x k-steps
+  constexpr int kStepsPV = (kBN / 16) * kDb;     // 16-key steps x d-blocks
+  constexpr int kSteps = kStepsQK > kStepsPV ? kStepsQK : kStepsPV;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const bool group_b = wave >= 4;
+
+  const int pred = it.pred_rows;
+  const int total = pred + it.own_rows;
+  const int n_tiles = (total + kBN - 1) / kBN;
+  const int64_t rs = a.row_stride;
+
+  const int64_t e = a.entry(it.b);
+  const T* qb = static_cast<const T*>(a.q) + e * a.q_bstride + (int64_t)it.h * D;
+  const T* kown = static_cast<const T*>(a.k) + e * a.kv_bstride + (int64_t)it.h * D;
+  const T* vown = static_cast<const T*>(a.v) + e * a.kv_bstride + (int64_t)it.h * D;
+  const T* kpre = kown;
+  const T* vpre = vown;
+  if (pred > 0) {
+    const int64_t pi = a.entry(it.b - a.pred_shift) * a.p_bstride + (int64_t)it.h * D;
+    kpre = static_cast<const T*>(a.pk) + pi;
+    vpre = static_cast<const T*>(a.pv) + pi;
+  }
+
+  // ---- Q fragment: B operand of S^T = K.Q^T, one query row per lane column
+  const int qrow = it.q0 + wave * 32 + l32;
+  const bool qvalid = wave * 32 + l32 < it.q_rows;
+  u32x4_t qf[kKs];
+#pragma unroll
+  for (int ks = 0; ks < kKs; ++ks)
+    qf[ks] = qvalid ? Io<T>::load8(qb + (int64_t)qrow * rs + ks * 16 + hh * 8)
+                    : u32x4_t{0u, 0u, 0u, 0u};
+
+  // ---- per-lane global load map: LDS chunk c = wave*kCpw + i of a tile
+  // receives tile row c*kRowsPerKB + lane/kBlk, physical block lane%kBlk
+  auto lrow = [&](int i) __attribute__((always_inline)) {
+    return (wave * kCpw + i) * G::kRowsPerKB + lane / G::kBlk;
+  };
+  uint32_t koffs[kCpw], voffs[kCpw];
+#pragma unroll
+  for (int i = 0; i < kCpw; ++i) {
+    const int r = lrow(i);
+    const int pb = lane % G::kBlk;
+    koffs[i] = (uint32_t)((r * rs + ((pb ^ k_swz<D>(r)) * 8)) * sizeof(T));
+    voffs[i] = (uint32_t)((r * rs + ((pb ^ v_swz<D>(r)) * 8)) * sizeof(T));
+  }
+  // This wave's share of rows [t*kBN, (t+1)*kBN) of K (kV false) or V into
+  // the LDS tile at dst.
+  auto load_one = [&](int t, unsigned char* dst, auto v_tag) __attribute__((always_inline)) {
+    constexpr bool kV = decltype(v_tag)::value;
+    const T* pre = kV ? vpre : kpre;
+    const T* own = kV ? vown : kown;
+    const int r0 = t * kBN;
+    if constexpr (sizeof(T) == 2) {
+      if (r0 + kBN <= pred || (r0 >= pred && r0 + kBN <= total)) {
+        const bool in_pred = r0 + kBN <= pred;
+        const char* base = reinterpret_cast<const char*>(
+            (in_pred ? pre : own) + (int64_t)(in_pred ? r0 : r0 - pred) * rs);
+#pragma unroll
+        for (int i = 0; i < kCpw; ++i)
+          load_lds16_async(base, kV ? voffs[i] : koffs[i], dst + (wave * kCpw + i) * 1024);
+      } else {
+        // straddling or ragged tile: rows past the end re-read the last row
+#pragma unroll
+        for (int i = 0; i < kCpw; ++i) {
+          const int r = lrow(i);
+          int j = r0 + r;
+          j = j < total ? j : total - 1;
+          const int blk = (lane % G::kBlk) ^ (kV ? v_swz<D>(r) : k_swz<D>(r));
+          const T* src = j < pred ? pre + (int64_t)j * rs : own + (int64_t)(j - pred) * rs;
+          load_lds16_async(src + blk * 8, dst + (wave * kCpw + i) * 1024);
+        }
+      }
+    } else {
+      // fp32 storage: convert to bf16 in registers, same LDS layout
+#pragma unroll
+      for (int i = 0; i < kCpw; ++i) {
+        const int r = lrow(i);
+        int j = r0 + r;
+        j = j < total ? j : total - 1;
+        const int blk = (lane % G::kBlk) ^ (kV ? v_swz<D>(r) : k_swz<D>(r));
+        const T* src = j < pred ? pre + (int64_t)j * rs : own + (int64_t)(j - pred) * rs;
+        *reinterpret_cast<u32x4_t*>(dst + (wave * kCpw + i) * 1024 + lane * 16) =
+            Io<T>::load8(src + blk * 8);
+      }
+    }
+  };
+  // ring slot byte offsets; tile g of K in slot g & 3, of V in slot 4 + (g & 3)
+  auto kslot = [&](int g) __attribute__((always_inline)) { return (uint32_t)(g & 3) * G::kTileBytes; };
+  auto vslot = [&](int g) __attribute__((always_inline)) {
+    return (uint32_t)(4 + (g & 3)) * G::kTileBytes;
+  };
+  // group g of loads: K(g) and V(g-1), whichever exist
+  auto issue = [&](int g) __attribute__((always_inline)) {
+    if (g < n_tiles) load_one(g, smem + kslot(g), std::false_type{});
+    if (g >= 1 && g <= n_tiles) load_one(g - 1, smem + vslot(g - 1), std::true_type{});
+  };
+  auto group_loads = [&](int g) __attribute__((always_inline)) {
+    return kCpw * ((g < n_tiles ? 1 : 0) + (g >= 1 && g <= n_tiles ? 1 : 0));
+  };
+  // waits until at most `left` of this wave's loads are in flight
+  auto wait_left = [&](int left) __attribute__((always_inline)) {
+    if (left <= 0)
+      wait_vmem();
+    else if (left <= kCpw)
+      wait_vmem_le<kCpw>();
+    else
+      wait_vmem_le<2 * kCpw>();
+  };
+
+  // ---- per-lane LDS read offsets (per-lane base + immediates, as in
+  // attn_kernel.h): K read of k-step ks for key row l32 of a 32-key block; V
+  // transposing reads of d-block db, lo/hi half w2
+  uint32_t koff_lds[kKs];
+  {
+    const int x = l32 & (G::kBlk - 1);
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks)
+      koff_lds[ks] = (uint32_t)(l32 * G::kRowBytes +
+                                ((2 * (ks ^ (x >> 1)) + (hh ^ (x & 1))) << 4));
+  }
+  uint32_t voff_lds[kDb][2];
+  {
+    const int g1 = (lane >> 4) & 1;
+    const int j16 = lane & 15;
+#pragma unroll
+    for (int db = 0; db < kDb; ++db)
+#pragma unroll
+      for (int w2 = 0; w2 < 2; ++w2) {
+        const int r = 4 * hh + (j16 >> 2) + 8 * w2;
+        const int col = 32 * db + 16 * g1 + 4 * (j16 & 3);
+        voff_lds[db][w2] = v_off<D>(r, col >> 3) + ((col >> 2) & 1) * 8;
+      }
+  }
+
+  f32x16_t oacc[kDb];
+#pragma unroll
+  for (int db = 0; db < kDb; ++db) oacc[db] = f32x16_t{};
+  f32x16_t sacc[2];       // S^T of the current tile, two 32-key blocks
+  uint32_t pk[2][8];      // P^T of the previous tile as bf16 pairs
+  float m_run = 0.f;      // reference maximum (log2 domain)
+  // The softmax denominator l is summed by the matrix core: one extra MFMA
+  // per 16-key step with an all-ones A operand turns the P^T operand into its
+  // column sums (every row of the 32x32 result is l of the lane's query).  It
+  // sums the same bf16-rounded numerators the P.V product uses, and takes
+  // four vector instructions per score pair off the softmax phase.
+  f32x16_t lacc = f32x16_t{};
+  const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+  const uint32_t one_w = __builtin_bit_cast(uint32_t, one2);
+  const u32x4_t ones = {one_w, one_w, one_w, one_w};
+  const float s2 = a.scale_log2;
+
+  // Matrix phase of tile t: P.V of tile t-1 (kPV) and S of tile t (kQK), with
+  // K(t) at LDS byte offset k_at and V(t-1) at v_at.  The two MFMA streams
+  // are interleaved step by step; the LDS reads run two steps ahead.
+  auto matrix_phase = [&](uint32_t k_at, uint32_t v_at, auto pv_tag, auto qk_tag)
+      __attribute__((always_inline)) {
+    constexpr bool kPV = decltype(pv_tag)::value;
+    constexpr bool kQK = decltype(qk_tag)::value;
+    const CA_LDS unsigned char* kl = (const CA_LDS unsigned char*)smem + k_at;
+    const CA_LDS unsigned char* vl = (const CA_LDS unsigned char*)smem + v_at;
+    // QK step i: key block i & 1, k-step i >> 1; PV step i: 16-key step
+    // i / kDb, d-block i % kDb
+    auto read_k = [&](int i) __attribute__((always_inline)) {
+      return *(CA_LDS const u32x4_t*)(kl + koff_lds[i >> 1] + (i & 1) * 32 * G::kRowBytes);
+    };
+    auto read_v = [&](int i) __attribute__((always_inline)) {
+      const int db = i % kDb;
+      const uint32_t imm = 16 * (i / kDb) * G::kRowBytes;
+      const i16x4_t lo =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((CA_LDS i16x4_t*)(vl + voff_lds[db][0] + imm));
+      const i16x4_t hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((CA_LDS i16x4_t*)(vl + voff_lds[db][1] + imm));
+      const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
+      const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
+      return u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
+    };
+    u32x4_t kf[3], vf[3];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if constexpr (kQK) kf[i] = read_k(i);
+      if constexpr (kPV) vf[i] = read_v(i);
+    }
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+      if constexpr (kQK) {
+        if (i + 2 < kStepsQK) kf[(i + 2) % 3] = read_k(i + 2);
+      }
+      if constexpr (kPV) {
+        if (i + 2 < kStepsPV) vf[(i + 2) % 3] = read_v(i + 2);
+      }
+      if constexpr (kQK) {
+        if (i < kStepsQK) {
+          const int kb2 = i & 1, ks = i >> 1;
+          sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, kf[i % 3]), __builtin_bit_cast(bf16x8_t, qf[ks]),
+              ks == 0 ? f32x16_t{} : sacc[kb2], 0, 0, 0);
+        }
+      }
+      if constexpr (kPV) {
+        if (i < kStepsPV) {
+          const int s = i / kDb, db = i % kDb;
+          const u32x4_t pb = {pk[s >> 1][(s & 1) * 4 + 0], pk[s >> 1][(s & 1) * 4 + 1],
+                              pk[s >> 1][(s & 1) * 4 + 2], pk[s >> 1][(s & 1) * 4 + 3]};
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, vf[i % 3]), __builtin_bit_cast(bf16x8_t, pb), oacc[db],
+              0, 0, 0);
+          if (db == kDb - 1)
+            lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ones),
+                                                           __builtin_bit_cast(bf16x8_t, pb), lacc,
+                                                           0, 0, 0);
+        }
+      }
+      // one step at a time: the scheduler would otherwise start most of the
+      // phase's LDS reads at once and run out of registers
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Softmax phase of tile t: numerators of the scores in sacc into pk and l
+  // (with kFirst, the reference maximum first; with a mask, keys >= total get
+  // P = 0).  Keys past the end of a ragged tile re-read the last key row, so
+  // they repeat an existing score and never raise the maximum.
+  auto softmax_phase = [&](int t, auto first_tag, auto mask_tag) __attribute__((always_inline)) {
+    if constexpr (decltype(first_tag)::value) {
+      float t8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int kb2 = i >> 2, j = (i & 3) * 4;
+        t8[i] = fmaxf(fmaxf(sacc[kb2][j], sacc[kb2][j + 1]), fmaxf(sacc[kb2][j + 2], sacc[kb2][j + 3]));
+      }
+      const float mx = fmaxf(fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3])),
+                             fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7])));
+      m_run = fmaxf(mx, other_half(mx)) * s2;
+    }
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][2 * i], s2, -m_run));
+        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][2 * i + 1], s2, -m_run));
+        if constexpr (decltype(mask_tag)::value) {
+          const int key0 = t * kBN + kb2 * 32 + 8 * ((2 * i) >> 2) + 4 * hh + ((2 * i) & 3);
+          if (key0 >= total) p0 = 0.f;
+          if (key0 + 1 >= total) p1 = 0.f;
+        }
+        pk[kb2][i] = pack_bf16(p0, p1);
+      }
+  };
+
+  // Barrier at the end of a matrix phase (the scores cross it) and at the end
+  // of a softmax phase (the numerators cross it).
+  auto end_matrix = [&]() __attribute__((always_inline)) {
+    pin(sacc[0]);
+    pin(sacc[1]);
+    wg_barrier();
+    pin(sacc[0]);
+    pin(sacc[1]);
+  };
+  auto end_softmax = [&]() __attribute__((always_inline)) {
+    pin(pk[0]);
+    pin(pk[1]);
+    wg_barrier();
+    pin(pk[0]);
+    pin(pk[1]);
+  };
+
+  // One tile: matrix phase (P.V of tile t-1 unless kFirst, S of tile t), then
+  // the softmax phase, with the loads of group t+3 started in it.
+  auto step = [&](int t, auto first_tag, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool kFirst = decltype(first_tag)::value;
+    // the matrix phase issues at the higher wave priority, so the SIMD picks
+    // this wave's MFMAs and LDS reads over the other wave's softmax
+    __builtin_amdgcn_s_setprio(3);
+    matrix_phase(kslot(t), vslot(t - 1), std::integral_constant<bool, !kFirst>{}, std::true_type{});
+    __builtin_amdgcn_s_setprio(0);
+    wait_left(group_loads(t + 2));
+    end_matrix();
+    softmax_phase(t, first_tag, mask_tag);
+    issue(t + 3);
+    end_softmax();
+  };
+
+  // ---- prologue: K(0) lands, groups 1 and 2 start
+  load_one(0, smem + kslot(0), std::false_type{});
+  wait_vmem();
+  wg_barrier();
+  issue(1);
+  issue(2);
+  if (group_b) wg_barrier();  // group B runs one phase behind group A
+
+  // ---- tiles 0 .. n-1 (the last one masked), then P.V of tile n-1
+  if (n_tiles == 1) {
+    step(0, std::true_type{}, Mask{});
+  } else {
+    step(0, std::true_type{}, NoMask{});
+    for (int t = 1; t + 1 < n_tiles; ++t) step(t, std::false_type{}, NoMask{});
+    step(n_tiles - 1, std::false_type{}, Mask{});
+  }
+  matrix_phase(0u, vslot(n_tiles - 1), std::true_type{}, std::false_type{});
+  if (!group_b) wg_barrier();  // matches group B's first barrier
+
+  // ---- epilogue: overflow check over the workgroup (this barrier also joins
+  // the two groups), then normalise and store this lane's query row
+  const float l_tot = lacc[0];
+  float acc = l_tot;
+#pragma unroll
+  for (int db = 0; db < kDb; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc += oacc[db][i];
+  T* ob = static_cast<T*>(a.o) + e * a.o_bstride + (int64_t)it.h * D;
+  if (__syncthreads_or(!__builtin_isfinite(acc))) {
+    if (tid == 0) ob[(int64_t)it.q0 * rs] = overflow_marker<T>();
+    return;
+  }
+  const float inv = 1.0f / l_tot;
+  if (qvalid) {
+    T* orow = ob + (int64_t)qrow * rs;
+#pragma unroll
+    for (int db = 0; db < kDb; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * hh;
+        Io<T>::store4(orow + d0, oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
+                      oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+      }
+  }
+}
+
+// Main pass, 256-row work items on the ping-pong schedule.
+template <int D, typename T>
+__global__ __launch_bounds__(512, 1) void chunk_attn_fwd_pingpong(KernelArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const Item it = decode(a.plan, slot_to_work(blockIdx.x, a.plan.n_items, a.plan.n_xcd));
+  attn_item_pingpong<D, T>(a, it, smem);
+}
+
+}  // namespace chunkattn

@@ -3,6 +3,7 @@
 // kernel launch.  No allocation happens on the hot calls.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -11,6 +12,7 @@
 #include <string>
 
 #include "attn_kernel.h"
+#include "attn_pingpong.h"
 #include "chunkattn.h"
 #include "fifo.h"
 #include "noise.h"
@@ -164,6 +166,10 @@ int validate_full(std::string* err, const void* q, const void* k, const void* v,
 
 // Every kernel configuration the host can launch, instantiated explicitly.
 namespace chunkattn {
+template __global__ void chunk_attn_fwd_pingpong<128, __bf16>(KernelArgs);
+template __global__ void chunk_attn_fwd_pingpong<128, float>(KernelArgs);
+template __global__ void chunk_attn_fwd_pingpong<64, __bf16>(KernelArgs);
+template __global__ void chunk_attn_fwd_pingpong<64, float>(KernelArgs);
 template __global__ void chunk_attn_fwd<128, __bf16, 4>(KernelArgs);
 template __global__ void chunk_attn_recheck<128, __bf16, 4>(KernelArgs);
 template __global__ void chunk_attn_fwd<128, float, 4>(KernelArgs);
@@ -172,25 +178,47 @@ template __global__ void chunk_attn_fwd<64, __bf16, 4>(KernelArgs);
 template __global__ void chunk_attn_recheck<64, __bf16, 4>(KernelArgs);
 template __global__ void chunk_attn_fwd<64, float, 4>(KernelArgs);
 template __global__ void chunk_attn_recheck<64, float, 4>(KernelArgs);
-template __global__ void chunk_attn_fwd<128, __bf16, 8>(KernelArgs);
 template __global__ void chunk_attn_recheck<128, __bf16, 8>(KernelArgs);
-template __global__ void chunk_attn_fwd<128, float, 8>(KernelArgs);
 template __global__ void chunk_attn_recheck<128, float, 8>(KernelArgs);
-template __global__ void chunk_attn_fwd<64, __bf16, 8>(KernelArgs);
 template __global__ void chunk_attn_recheck<64, __bf16, 8>(KernelArgs);
-template __global__ void chunk_attn_fwd<64, float, 8>(KernelArgs);
 template __global__ void chunk_attn_recheck<64, float, 8>(KernelArgs);
 }  // namespace chunkattn
 
 namespace {
 
-// W waves x 32 query rows per work item, synchronous schedule: the
-// fixed-maximum pass, then the overflow recheck on the same stream.
+// The ping-pong kernel uses more than the default 64 KB of dynamic LDS; the
+// limit is raised once per device (bit d of `done` for device d).
+template <int D, typename T>
+hipError_t allow_pingpong_lds() {
+  static std::atomic<uint64_t> done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunkattn::chunk_attn_fwd_pingpong<D, T>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)chunkattn::kPingPongLdsBytes<D>);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
+// The fixed-maximum pass (W = 8: 256-row work items on the ping-pong
+// schedule; W = 4: 128-row items on the synchronous one), then the overflow
+// recheck (synchronous schedule, running maximum) on the same stream.
 template <int D, typename T, int W>
 hipError_t launch_t(const KernelArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)a.plan.n_items);
   constexpr uint32_t kLds = chunkattn::kSyncLdsBytes<D>;
-  hipLaunchKernelGGL((chunkattn::chunk_attn_fwd<D, T, W>), grid, dim3(64 * W), kLds, stream, a);
+  if constexpr (W == 8) {
+    const hipError_t el = allow_pingpong_lds<D, T>();
+    if (el != hipSuccess) return el;
+    hipLaunchKernelGGL((chunkattn::chunk_attn_fwd_pingpong<D, T>), grid, dim3(512),
+                       chunkattn::kPingPongLdsBytes<D>, stream, a);
+  } else {
+    hipLaunchKernelGGL((chunkattn::chunk_attn_fwd<D, T, W>), grid, dim3(64 * W), kLds, stream,
+                       a);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((chunkattn::chunk_attn_recheck<D, T, W>), grid, dim3(64 * W), kLds, stream,

@@ -200,14 +200,19 @@ def test_device_plan_equals_host_plan(flags):
         np.testing.assert_array_equal(dev, host)
 
 
-def test_block_sizes_give_identical_bits():
-    """A wave computes the same 32 query rows the same way whichever work-item
-    size groups it, so the two launch configurations agree bit for bit."""
+def test_block_sizes_agree():
+    """The two launch configurations run different schedules (128-row items:
+    the synchronous one, l summed on the vector ALU; 256-row items: the
+    ping-pong one, l summed by the matrix core), so their sums round in a
+    different order: they agree to a few bf16 rounding steps, well inside the
+    parity bar each of them meets against the oracle."""
     q, k, v = synth.queue_inputs(5, 700, 3, 128, seed=14, device=DEV, k_rho=0.9)
     cache = synth.build_cache(k, v)
-    a = run_queue(q, k, v, cache, flags=ca.FLAG_BLOCK128)
-    b = run_queue(q, k, v, cache, flags=ca.FLAG_BLOCK256)
-    assert torch.equal(a, b)
+    a = run_queue(q, k, v, cache, flags=ca.FLAG_BLOCK128).float()
+    b = run_queue(q, k, v, cache, flags=ca.FLAG_BLOCK256).float()
+    d = (a - b).abs()
+    say("block 128 vs 256: max", d.max().item(), "mean", d.mean().item())
+    assert d.max().item() <= 4e-3 and d.mean().item() <= 2e-4
 
 
 # -------------------------------------------------------------------- full attention

@@ -86,6 +86,11 @@ struct KernelArgs {
   // predecessor in place from the slot of b - 1.  0: batch b is entry b.
   int ring_slots;
   int ring_tail;
+  // Work queue of the persistent launch (null: one workgroup per work item,
+  // item = plan_slot_work(blockIdx.x)).  Words 0 .. n_xcd-1 count the claims on
+  // each die's share (see claim_word_item), word n_xcd the finished workgroups;
+  // all zero at launch, and the last workgroup to finish zeroes them again.
+  unsigned long long* queue;
 
   // Physical entry of batch index b (b > -ring_slots).
   __host__ __device__ __forceinline__ int64_t entry(int b) const {
@@ -615,7 +620,7 @@ __device__ __forceinline__ void attn_item_sync(const KernelArgs& a, const Item& 
 template <int D, typename T, int W>
 __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  const Item it = decode(a.plan, slot_to_work(blockIdx.x, a.plan.n_items, a.plan.n_xcd));
+  const Item it = decode(a.plan, plan_slot_work(a.plan, blockIdx.x));
   attn_item_sync<D, T, W, true>(a, it, smem);
 }
 
@@ -625,7 +630,7 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
 template <int D, typename T, int W>
 __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_recheck(KernelArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  const Item it = decode(a.plan, slot_to_work(blockIdx.x, a.plan.n_items, a.plan.n_xcd));
+  const Item it = decode(a.plan, plan_slot_work(a.plan, blockIdx.x));
   const T first = static_cast<const T*>(a.o)[a.entry(it.b) * a.o_bstride + (int64_t)it.q0 * a.row_stride +
                                               (int64_t)it.h * D];
   if (!__builtin_isnan((float)first)) return;
@@ -633,11 +638,11 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_recheck(KernelArgs a
 }
 
 // Writes the decoded work item of every workgroup slot (7 ints each), using
-// the same slot_to_work/decode as the attention kernel.
+// the same plan_slot_work/decode as the attention kernel.
 __global__ void plan_dump(Plan p, int* out, int64_t cap) {
   const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (slot >= p.n_items || slot >= cap) return;
-  const Item it = decode(p, slot_to_work(slot, p.n_items, p.n_xcd));
+  const Item it = decode(p, plan_slot_work(p, slot));
   int* r = out + slot * 7;
   r[0] = it.b;
   r[1] = it.h;

@@ -65,9 +65,12 @@ __device__ __forceinline__ void pin(float (&l)[4]) {
   asm volatile("" : "+v"(l[0]), "+v"(l[1]), "+v"(l[2]), "+v"(l[3]));
 }
 
-template <int D, typename T>
+// after_prologue() runs once in every thread, after the prologue's barrier
+// (every wave has started the item by then).
+template <int D, typename T, typename AfterPrologue>
 __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const Item& it,
-                                                   unsigned char* smem) {
+                                                   unsigned char* smem,
+                                                   AfterPrologue&& after_prologue) {
   using G = Geo<D>;
   constexpr int W = 8;
   constexpr int kCpw = G::kChunks / W;  // 1 KB load chunks per wave per matrix
@@ -101,6 +104,17 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
     kpre = static_cast<const T*>(a.pk) + pi;
     vpre = static_cast<const T*>(a.pv) + pi;
   }
+  // the four segment bases are wave-uniform: keep them in scalar registers
+  auto uniform_ptr = [](const T* p) __attribute__((always_inline)) {
+    const uint64_t b = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    return (const T*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+  };
+  kpre = uniform_ptr(kpre);
+  vpre = uniform_ptr(vpre);
+  kown = uniform_ptr(kown);
+  vown = uniform_ptr(vown);
 
   // ---- Q fragment: B operand of S^T = K.Q^T, one query row per lane column
   const int qrow = it.q0 + wave * 32 + l32;
@@ -365,6 +379,7 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
   load_one(0, smem + kslot(0), std::false_type{});
   wait_vmem();
   wg_barrier();
+  after_prologue();
   issue(1);
   issue(2);
   if (group_b) wg_barrier();  // group B runs one phase behind group A
@@ -407,12 +422,80 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
   }
 }
 
-// Main pass, 256-row work items on the ping-pong schedule.
+// Main pass, 256-row work items on the ping-pong schedule, as a persistent
+// launch: one workgroup per CU takes work items from its die's queue (the
+// die's launch-slot share of plan_slot_work, longest items first) until it is
+// empty, then from the back of the other dies' queues, so a die that runs at a
+// lower clock ends up with less work and a new item needs no workgroup
+// launch.  Thread 0 starts the claim of the next item before the current one;
+// the atomic's latency overlaps the first tile's load, whose wait (vmcnt 0)
+// also covers it, and the result goes to LDS after the prologue's barrier.
 template <int D, typename T>
 __global__ __launch_bounds__(512, 1) void chunk_attn_fwd_pingpong(KernelArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  const Item it = decode(a.plan, slot_to_work(blockIdx.x, a.plan.n_items, a.plan.n_xcd));
-  attn_item_pingpong<D, T>(a, it, smem);
+  __shared__ long long next_item;  // >= 0 item, -1 none left, -2 claim again
+  __shared__ int used_up;          // thread 0: dies (from our own on) found empty
+  const int nx = a.plan.n_xcd;
+  // the die this workgroup runs on (hardware register XCC_ID, bits 3:0)
+  const int die = (int)(__builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) % (unsigned)nx);
+  auto die_at = [&](int k) __attribute__((always_inline)) {
+    return die + k < nx ? die + k : die + k - nx;
+  };
+  // claim word increment: the own die's queue from the front, others' from the back
+  auto step_of = [](int k) __attribute__((always_inline)) { return k == 0 ? 1ull : (1ull << 32); };
+  // thread 0: claim with one atomic per die until one has work left
+  auto claim_sync = [&]() __attribute__((always_inline)) {
+    int k = used_up;
+    long long w = -1;
+    for (; k < nx; ++k) {
+      const unsigned long long old = atomicAdd(&a.queue[die_at(k)], step_of(k));
+      w = claim_word_item(a.plan, die_at(k), old, k > 0);
+      if (w >= 0) break;
+    }
+    used_up = k;
+    next_item = w;
+  };
+  if (threadIdx.x == 0) {
+    used_up = 0;
+    claim_sync();
+  }
+  __syncthreads();
+  long long w = next_item;
+  while (w >= 0) {
+    unsigned long long ticket = 0;
+    int k = nx;
+    if (threadIdx.x == 0) {
+      k = used_up;
+      if (k < nx) ticket = atomicAdd(&a.queue[die_at(k)], step_of(k));
+    }
+    attn_item_pingpong<D, T>(a, decode(a.plan, w), smem, [&]() __attribute__((always_inline)) {
+      if (threadIdx.x == 0) {
+        long long nw = -1;
+        if (k < nx) {
+          nw = claim_word_item(a.plan, die_at(k), ticket, k > 0);
+          if (nw < 0) nw = -2;
+        }
+        next_item = nw;
+      }
+    });
+    wg_barrier();
+    w = next_item;
+    if (w == -2) {
+      wg_barrier();  // every wave has read next_item before thread 0 rewrites it
+      if (threadIdx.x == 0) {
+        used_up = used_up + 1;
+        claim_sync();
+      }
+      wg_barrier();
+      w = next_item;
+    }
+  }
+  // the last workgroup to finish leaves the queue zeroed for the next launch
+  if (threadIdx.x == 0) {
+    const unsigned long long done = atomicAdd(&a.queue[nx], 1ull);
+    if (done == (unsigned long long)gridDim.x - 1)
+      for (int x = 0; x <= nx; ++x) atomicExch(&a.queue[x], 0ull);
+  }
 }
 
 }  // namespace chunkattn

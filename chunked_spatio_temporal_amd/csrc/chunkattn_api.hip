@@ -17,11 +17,20 @@
 #include "fifo.h"
 #include "noise.h"
 
+// Work-queue slots of a context: each call of the persistent (256-row) main
+// pass takes the next slot, so up to kQueueSlots calls may be in flight on
+// different streams at once.  A slot is kQueueWords 64-bit words (one claim
+// word per die, one finished-workgroup counter), zero between launches.
+constexpr int kQueueSlots = 64;
+constexpr int kQueueWords = 16;
+
 struct chunkattn_ctx {
   int device = 0;
   int n_cu = 0;
   int n_xcd = 1;
   int waves = 8;  // waves per workgroup; a work item covers 32 * waves query rows
+  unsigned long long* queue = nullptr;  // device, kQueueSlots * kQueueWords words
+  std::atomic<unsigned> next_slot{0};
   std::string arch;
   std::string err;
 };
@@ -206,14 +215,18 @@ hipError_t allow_pingpong_lds() {
 // The fixed-maximum pass (W = 8: 256-row work items on the ping-pong
 // schedule; W = 4: 128-row items on the synchronous one), then the overflow
 // recheck (synchronous schedule, running maximum) on the same stream.
+// W = 8: the main pass is persistent, n_persist workgroups (one per CU) share
+// the work items through the work queue a.queue.
 template <int D, typename T, int W>
-hipError_t launch_t(const KernelArgs& a, hipStream_t stream) {
+hipError_t launch_t(const KernelArgs& a, int n_persist, hipStream_t stream) {
   const dim3 grid((unsigned)a.plan.n_items);
   constexpr uint32_t kLds = chunkattn::kSyncLdsBytes<D>;
   if constexpr (W == 8) {
+    if (!a.queue || n_persist < 1) return hipErrorInvalidValue;
     const hipError_t el = allow_pingpong_lds<D, T>();
     if (el != hipSuccess) return el;
-    hipLaunchKernelGGL((chunkattn::chunk_attn_fwd_pingpong<D, T>), grid, dim3(512),
+    hipLaunchKernelGGL((chunkattn::chunk_attn_fwd_pingpong<D, T>), dim3((unsigned)n_persist),
+                       dim3(512),
                        chunkattn::kPingPongLdsBytes<D>, stream, a);
   } else {
     hipLaunchKernelGGL((chunkattn::chunk_attn_fwd<D, T, W>), grid, dim3(64 * W), kLds, stream,
@@ -227,18 +240,19 @@ hipError_t launch_t(const KernelArgs& a, hipStream_t stream) {
 }
 
 template <int W>
-hipError_t launch_w(const KernelArgs& a, int head_dim, int dtype, hipStream_t stream) {
+hipError_t launch_w(const KernelArgs& a, int n_persist, int head_dim, int dtype,
+                    hipStream_t stream) {
   if (head_dim == 128)
-    return dtype == CHUNKATTN_BF16 ? launch_t<128, __bf16, W>(a, stream)
-                                   : launch_t<128, float, W>(a, stream);
-  return dtype == CHUNKATTN_BF16 ? launch_t<64, __bf16, W>(a, stream)
-                                 : launch_t<64, float, W>(a, stream);
+    return dtype == CHUNKATTN_BF16 ? launch_t<128, __bf16, W>(a, n_persist, stream)
+                                   : launch_t<128, float, W>(a, n_persist, stream);
+  return dtype == CHUNKATTN_BF16 ? launch_t<64, __bf16, W>(a, n_persist, stream)
+                                 : launch_t<64, float, W>(a, n_persist, stream);
 }
 
-hipError_t launch(const KernelArgs& a, int waves, int head_dim, int dtype,
+hipError_t launch(const KernelArgs& a, int waves, int n_persist, int head_dim, int dtype,
                   hipStream_t stream) {
-  return waves == 4 ? launch_w<4>(a, head_dim, dtype, stream)
-                    : launch_w<8>(a, head_dim, dtype, stream);
+  return waves == 4 ? launch_w<4>(a, n_persist, head_dim, dtype, stream)
+                    : launch_w<8>(a, n_persist, head_dim, dtype, stream);
 }
 
 // Makes the context's device current for the duration of a call.
@@ -255,11 +269,21 @@ struct DeviceGuard {
   }
 };
 
-int run(chunkattn_ctx* ctx, const KernelArgs& a, int head_dim, int dtype, void* stream) {
+int run(chunkattn_ctx* ctx, const KernelArgs& args, int head_dim, int dtype, void* stream) {
   DeviceGuard g(ctx->device);
   if (!g.ok) return set_err(&ctx->err, CHUNKATTN_EDEVICE, "cannot make device %d current",
                             ctx->device);
-  const hipError_t e = launch(a, ctx->waves, head_dim, dtype, static_cast<hipStream_t>(stream));
+  KernelArgs a = args;
+  a.queue = nullptr;
+  if (ctx->waves == 8) {
+    // one claim word per die and the finished count must fit in a slot
+    if (a.plan.n_xcd >= kQueueWords) a.plan.n_xcd = 1;
+    const unsigned slot = ctx->next_slot.fetch_add(1, std::memory_order_relaxed) % kQueueSlots;
+    a.queue = ctx->queue + (size_t)slot * kQueueWords;
+  }
+  const int n_persist = (int)(a.plan.n_items < ctx->n_cu ? a.plan.n_items : ctx->n_cu);
+  const hipError_t e =
+      launch(a, ctx->waves, n_persist, head_dim, dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return set_err(&ctx->err, CHUNKATTN_ELAUNCH, "kernel launch failed: %s",
                    hipGetErrorString(e));
@@ -311,11 +335,33 @@ int chunkattn_create(chunkattn_ctx** out, int device_ordinal, unsigned flags) {
           hipSuccess &&
       xcc > 0)
     ctx->n_xcd = xcc;
+  if (ctx->waves == 8) {
+    // the work queue of the persistent main pass, zeroed once here
+    DeviceGuard g(device_ordinal);
+    const size_t bytes = sizeof(unsigned long long) * kQueueSlots * kQueueWords;
+    void* q = nullptr;
+    if (!g.ok || hipMalloc(&q, bytes) != hipSuccess) {
+      delete ctx;
+      return set_err(&g_thread_err, CHUNKATTN_EDEVICE, "device %d: work-queue allocation failed",
+                     device_ordinal);
+    }
+    if (hipMemset(q, 0, bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+      (void)hipFree(q);
+      delete ctx;
+      return set_err(&g_thread_err, CHUNKATTN_EDEVICE, "device %d: work-queue setup failed",
+                     device_ordinal);
+    }
+    ctx->queue = static_cast<unsigned long long*>(q);
+  }
   *out = ctx;
   return CHUNKATTN_OK;
 }
 
 int chunkattn_destroy(chunkattn_ctx* ctx) {
+  if (ctx && ctx->queue) {
+    DeviceGuard g(ctx->device);
+    (void)hipFree(ctx->queue);
+  }
   delete ctx;
   return CHUNKATTN_OK;
 }
@@ -468,7 +514,7 @@ int chunkattn_window_plan_debug(int chunk_len, int n_chunks, int heads, int n_xc
   *n_items = p.n_items;
   for (int64_t slot = 0; slot < p.n_items && slot < cap; ++slot) {
     const chunkattn::Item it =
-        chunkattn::decode(p, chunkattn::slot_to_work(slot, p.n_items, p.n_xcd));
+        chunkattn::decode(p, chunkattn::plan_slot_work(p, slot));
     int* r = items + slot * 7;
     r[0] = it.b;
     r[1] = it.h;
@@ -709,7 +755,7 @@ int chunkattn_plan_debug(int chunk_len, int n_chunks, int heads, int n_xcd, int 
   *n_items = p.n_items;
   for (int64_t slot = 0; slot < p.n_items && slot < cap; ++slot) {
     const chunkattn::Item it =
-        chunkattn::decode(p, chunkattn::slot_to_work(slot, p.n_items, p.n_xcd));
+        chunkattn::decode(p, chunkattn::plan_slot_work(p, slot));
     int* r = items + slot * 7;
     r[0] = it.b;
     r[1] = it.h;

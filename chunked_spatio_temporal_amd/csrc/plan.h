@@ -16,9 +16,14 @@
 // (b, h, t) with t fastest, so consecutive items share one chunk/head's K/V.
 //
 // Die-aware launch order.  Workgroup ids are handed to the accelerator dies
-// round-robin (id % n_xcd).  slot_to_work() renumbers so that die x processes
-// one contiguous range of work items; the query tiles of one (chunk, head) then
-// run together on one die and share that die's L2 copy of the K/V tiles.
+// round-robin (id % n_xcd), and each die runs its own ids in increasing order.
+// slot_to_work() renumbers so that every die gets an equal share of the long
+// items (those with a predecessor) and an equal share of the short ones, each
+// share a contiguous range of the work order, long share first.  The query
+// tiles of one (chunk, head) then run together on one die and share that die's
+// L2 copy of the K/V tiles, and all dies walk about the same number of key
+// rows (one contiguous range per die would leave the short items of chunk 0
+// to the last die, which then idles for half the launch).
 #pragma once
 
 #include <stdint.h>
@@ -80,16 +85,49 @@ CA_HD Plan make_plan(int n_batch, int first_pred, int heads, int lq, int lown, i
   return make_plan(n_batch, first_pred, heads, lq, lown, lpred, bm, n_xcd, lq, lown);
 }
 
-// Launch slot (workgroup id) -> work index.  A bijection on [0, n): die x
-// (= slot % n_xcd) gets the contiguous range of work indices that starts at
-// x*per + min(x, extra), where per = n / n_xcd and the first `extra` dies
-// take one more.
-CA_HD int64_t slot_to_work(int64_t slot, int64_t n, int n_xcd) {
+// First index of die x's share when m items are split over n_xcd dies as
+// evenly as possible (the first m % n_xcd dies take one more).
+CA_HD int64_t die_share_start(int64_t m, int64_t x, int n_xcd) {
+  const int64_t per = m / n_xcd, extra = m % n_xcd;
+  return x * per + (x < extra ? x : extra);
+}
+
+// Launch slot (workgroup id) -> work index, a bijection on [0, n).  Work
+// indices [0, n_first) are the long items, [n_first, n) the short ones.  Die x
+// (= slot % n_xcd) owns the slots x, x + n_xcd, ...; the first F_x of them take
+// its share of the long items and the rest a contiguous range of short items.
+// The short count of a die, S_x - F_x, is never negative: S_x and F_x are
+// even splits of n >= n_first.
+CA_HD int64_t slot_to_work(int64_t slot, int64_t n, int64_t n_first, int n_xcd) {
   if (n_xcd <= 1) return slot;
-  const int64_t per = n / n_xcd, extra = n % n_xcd;
   const int64_t x = slot % n_xcd, local = slot / n_xcd;
-  // slots of the last round exist only for dies x < extra
-  return x * per + (x < extra ? x : extra) + local;
+  const int64_t s0 = die_share_start(n, x, n_xcd);
+  const int64_t f0 = die_share_start(n_first, x, n_xcd);
+  const int64_t fx = die_share_start(n_first, x + 1, n_xcd) - f0;
+  if (local < fx) return f0 + local;
+  return n_first + (s0 - f0) + (local - fx);
+}
+
+// The work index of launch slot `slot` under plan p.
+CA_HD int64_t plan_slot_work(const Plan& p, int64_t slot) {
+  return slot_to_work(slot, p.n_items, p.n_items_pred, p.n_xcd);
+}
+
+// Persistent launch: each die x owns the work of its launch slots
+// x, x + n_xcd, ... (count die_share_start(n, x+1) - die_share_start(n, x)) as
+// a queue.  A claim word packs the claims taken from the front (low 32 bits,
+// by the die's own workgroups, longest items first) and from the back (high 32
+// bits, by workgroups of dies whose own queue is empty).  `old` is the word's
+// value before this claim added 1 to its half; the claim gets the queue
+// position front or count-1-back while front + back < count, so every item is
+// taken exactly once, and -1 once the queue is used up.
+CA_HD int64_t claim_word_item(const Plan& p, int x, unsigned long long old, bool from_back) {
+  const int64_t count = die_share_start(p.n_items, x + 1, p.n_xcd) -
+                        die_share_start(p.n_items, x, p.n_xcd);
+  const int64_t front = (int64_t)(old & 0xFFFFFFFFull), back = (int64_t)(old >> 32);
+  if (front + back >= count) return -1;
+  const int64_t pos = from_back ? count - 1 - back : front;
+  return plan_slot_work(p, x + pos * p.n_xcd);
 }
 
 CA_HD Item decode(const Plan& p, int64_t w) {

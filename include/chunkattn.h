@@ -39,11 +39,16 @@
  *
  * Ownership and asynchrony.  Every tensor pointer is device memory owned by the
  * caller and must stay valid until the stream work completes.  The library
- * owns only the context.  queue_step and full make no allocation: they
- * validate, enqueue one kernel on hip_stream (NULL = the legacy default
+ * owns only the context; a context of 256-row work items also owns an 8 KB
+ * device buffer, the work queue of its persistent main pass, allocated and
+ * zeroed by chunkattn_create.  queue_step and full make no allocation: they
+ * validate, enqueue the kernels on hip_stream (NULL = the legacy default
  * stream) and return; a device fault surfaces at the caller's next
  * synchronisation.  One context may be used by one host thread at a time;
- * separate contexts are independent.
+ * separate contexts are independent.  Each call of a 256-row context takes
+ * the next of 64 work-queue slots, which its last workgroup leaves zeroed:
+ * calls may be spread over several streams as long as at most 64 of them are
+ * in flight at once (calls on one stream never overlap).
  *
  * Errors.  Every call returns a chunkattn_status synchronously, before any
  * launch, for bad arguments; chunkattn_last_error() then holds a one-line
@@ -85,7 +90,8 @@ int chunkattn_block_rows(void);
  * ordinal is invalid.  `flags` is 0 (library default work-item size) or one of
  * CHUNKATTN_FLAG_BLOCK128 / CHUNKATTN_FLAG_BLOCK256; results do not depend on
  * it beyond fp32 rounding order.  On success *out owns the context; release it
- * with chunkattn_destroy.
+ * with chunkattn_destroy.  CHUNKATTN_EDEVICE also reports a failed allocation
+ * of the work queue (256-row contexts).
  */
 int chunkattn_create(chunkattn_ctx **out, int device_ordinal, unsigned flags);
 

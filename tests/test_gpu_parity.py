@@ -100,6 +100,52 @@ def test_deterministic_and_order_independent_of_stream_state():
     assert torch.equal(a, b)
 
 
+def test_work_queue_slots_reused_across_many_calls():
+    """The 256-row main pass is persistent and takes its items from a work
+    queue that the last workgroup zeroes again; a context cycles through 64
+    queue slots.  150 back-to-back calls (every slot used twice or more), each
+    into a NaN-filled output, all give the first call's bits: no item is
+    skipped or done twice after a slot is reused."""
+    ctx = ca.create(0, ca.FLAG_BLOCK256)
+    inputs = [synth.queue_inputs(4, 200, 3, 128, seed=s, device=DEV) for s in (21, 22)]
+    refs = []
+    for q, k, v in inputs:
+        refs.append(ca.queue_step(q, k, v, None, ctx=ctx))
+    torch.cuda.synchronize()
+    outs = []
+    for i in range(150):
+        q, k, v = inputs[i % 2]
+        o = torch.full_like(q, float("nan"))
+        ca.queue_step(q, k, v, None, out=o, ctx=ctx)
+        outs.append(o)
+    torch.cuda.synchronize()
+    say("calls", len(outs))
+    for i, o in enumerate(outs):
+        assert torch.equal(o, refs[i % 2]), f"call {i}"
+
+
+def test_work_queue_two_streams_interleaved():
+    """Calls of one context on two streams, launched alternately without
+    synchronisation, use distinct queue slots and match the serial results."""
+    ctx = ca.create(0, ca.FLAG_BLOCK256)
+    a_in = synth.queue_inputs(8, 700, 5, 128, seed=31, device=DEV)
+    b_in = synth.queue_inputs(3, 1000, 4, 64, seed=32, device=DEV)
+    ref_a = ca.queue_step(*a_in, None, ctx=ctx)
+    ref_b = ca.queue_step(*b_in, None, ctx=ctx)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for i in range(6):
+        for st, inp in ((s1, a_in), (s2, b_in)):
+            with torch.cuda.stream(st):
+                o = torch.full_like(inp[0], float("nan"))
+                ca.queue_step(*inp, None, out=o, ctx=ctx, stream=st)
+            outs.append(o)
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert torch.equal(o, ref_a if i % 2 == 0 else ref_b), f"launch {i}"
+
+
 def test_guard_bands_and_cache_slot0_never_read():
     n, L, H, D = 3, 150, 2, 128
     q, k, v = synth.queue_inputs(n, L, H, D, seed=8, device=DEV)

@@ -141,16 +141,21 @@ def test_queue_step_without_context_is_rejected():
 
 # ---------------------------------------------------------------------- plan
 
-def _slot_to_work_reference(n, n_xcd):
-    """Die x runs work items [start_x, start_x + count_x) in launch order."""
+def _slot_to_work_reference(n, n_xcd, n_first=0):
+    """Die x runs slots x, x + n_xcd, ... in order.  It takes an even share of
+    the long work items [0, n_first) (one contiguous piece), then as many short
+    items [n_first, n) as it has slots left, again one contiguous piece."""
     order = np.empty(n, np.int64)
-    per, extra = divmod(n, n_xcd)
-    start = 0
+    long_pieces = np.array_split(np.arange(n_first), n_xcd)
+    next_short = n_first
     for x in range(n_xcd):
-        count = per + (1 if x < extra else 0)
-        slots = np.arange(x, n, n_xcd)[:count]
-        order[slots] = np.arange(start, start + count)
-        start += count
+        slots = np.arange(x, n, n_xcd)
+        longs = long_pieces[x]
+        assert len(longs) <= len(slots)
+        shorts = np.arange(next_short, next_short + len(slots) - len(longs))
+        next_short += len(shorts)
+        order[slots] = np.r_[longs, shorts]
+    assert next_short == n
     return order
 
 
@@ -220,7 +225,8 @@ def test_window_plan_order_longest_first():
     items = ca.window_plan_debug(L, n, H, xcd)
     bm = ca.block_rows()
     nq, nq_last = -(-2 * L // bm), -(-L // bm)
-    by_work = items[np.argsort(_slot_to_work_reference(len(items), xcd))]
+    n_first = int((items[:, 5] > 0).sum())
+    by_work = items[np.argsort(_slot_to_work_reference(len(items), xcd, n_first))]
     # windows 1..n-2 (three segments), the last window, then window 0
     expect_c = np.r_[np.repeat(np.arange(1, n - 1), H * nq), np.full(H * nq_last, n - 1),
                      np.zeros(H * nq, int)]
@@ -242,7 +248,7 @@ def test_plan_order_longest_first_and_die_ranges():
     items = ca.plan_debug(L, n, H, xcd)
     nq = -(-L // ca.block_rows())
     # reconstruct the work index of every slot and check it is the reference bijection
-    order = _slot_to_work_reference(len(items), xcd)
+    order = _slot_to_work_reference(len(items), xcd, int((items[:, 5] > 0).sum()))
     by_work = items[np.argsort(order)]
     # work order: chunks 1..n-1 (two segments) first, chunk 0 last; t fastest
     expect_c = np.r_[np.repeat(np.arange(1, n), H * nq), np.zeros(H * nq, int)]
@@ -261,6 +267,34 @@ def test_slot_to_work_is_a_bijection(n_items, xcd):
     got = items[:, 2] // bm                      # tile index == work index here
     np.testing.assert_array_equal(got, _slot_to_work_reference(n_items, xcd))
     assert sorted(got.tolist()) == list(range(n_items))
+
+
+@pytest.mark.parametrize("bm", [128, 256])
+@pytest.mark.parametrize("L,n,H,xcd", [(97, 5, 3, 8), (128, 4, 2, 8), (300, 3, 7, 8),
+                                       (6240, 8, 40, 8), (6240, 8, 12, 8), (1000, 9, 5, 8),
+                                       (200, 2, 3, 3), (64, 7, 1, 8), (1, 2, 1, 8)])
+def test_die_order_is_the_two_class_split(L, n, H, xcd, bm):
+    """Queue plans with long (predecessor) and short items: the slot -> work map
+    is the reference two-class split, and every die walks about the same number
+    of key rows (within one long item of the others)."""
+    items = ca.plan_debug(L, n, H, xcd, bm)
+    n_first = int((items[:, 5] > 0).sum())
+    order = _slot_to_work_reference(len(items), xcd, n_first)
+    by_work = items[np.argsort(order)]
+    # work order: long items first
+    assert (by_work[:n_first, 5] > 0).all() and (by_work[n_first:, 5] == 0).all()
+    # the library's slots agree with the reference map item for item
+    c, h, q0 = by_work[:, 0], by_work[:, 1], by_work[:, 2]
+    nq = -(-L // bm)
+    work_key = (c * H + h) * nq + q0 // bm
+    pred_first = np.r_[np.arange(1, n), [0]] if n > 1 else np.array([0])
+    expect_key = np.concatenate([(cc * H + np.repeat(np.arange(H), nq)) * nq + np.tile(np.arange(nq), H)
+                                 for cc in pred_first])
+    np.testing.assert_array_equal(work_key, expect_key)
+    # balance: the dies' key-row totals differ by at most one long plus one short item
+    rows = (items[:, 5] + items[:, 6]).astype(np.int64)
+    per_die = np.array([rows[x::xcd].sum() for x in range(xcd)])
+    assert per_die.max() - per_die.min() <= 2 * L + L
 
 
 # ------------------------------------------------------- streaming queue (host)

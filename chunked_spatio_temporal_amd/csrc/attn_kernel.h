@@ -86,10 +86,11 @@ struct KernelArgs {
   // predecessor in place from the slot of b - 1.  0: batch b is entry b.
   int ring_slots;
   int ring_tail;
-  // Work queue of the persistent launch (null: one workgroup per work item,
-  // item = plan_slot_work(blockIdx.x)).  Words 0 .. n_xcd-1 count the claims on
-  // each die's share (see claim_word_item), word n_xcd the finished workgroups;
-  // all zero at launch, and the last workgroup to finish zeroes them again.
+  // Work queue of the persistent 256-row main pass (chunk_attn_fwd_pingpong;
+  // the other kernels take item plan_slot_work(blockIdx.x)).  Word x <
+  // n_xcd counts the claims on die x's share (claim_word_item), word n_xcd the
+  // finished workgroups; all zero at launch, and the last workgroup to finish
+  // zeroes them again.
   unsigned long long* queue;
 
   // Physical entry of batch index b (b > -ring_slots).

@@ -425,11 +425,11 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
 // Main pass, 256-row work items on the ping-pong schedule, as a persistent
 // launch: one workgroup per CU takes work items from its die's queue (the
 // die's launch-slot share of plan_slot_work, longest items first) until it is
-// empty, then from the back of the other dies' queues, so a die that runs at a
-// lower clock ends up with less work and a new item needs no workgroup
-// launch.  Thread 0 starts the claim of the next item before the current one;
-// the atomic's latency overlaps the first tile's load, whose wait (vmcnt 0)
-// also covers it, and the result goes to LDS after the prologue's barrier.
+// empty, then from the other dies' queues, so a die that runs at a lower clock
+// ends up with less work and a new item needs no workgroup launch.  Thread 0
+// starts the claim of the next item before the current one; the atomic's
+// latency overlaps the first tile's load, whose wait (vmcnt 0) also covers it,
+// and the result goes to LDS after the prologue's barrier.
 template <int D, typename T>
 __global__ __launch_bounds__(512, 1) void chunk_attn_fwd_pingpong(KernelArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -441,15 +441,13 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_fwd_pingpong(KernelArgs a) 
   auto die_at = [&](int k) __attribute__((always_inline)) {
     return die + k < nx ? die + k : die + k - nx;
   };
-  // claim word increment: the own die's queue from the front, others' from the back
-  auto step_of = [](int k) __attribute__((always_inline)) { return k == 0 ? 1ull : (1ull << 32); };
   // thread 0: claim with one atomic per die until one has work left
   auto claim_sync = [&]() __attribute__((always_inline)) {
     int k = used_up;
     long long w = -1;
     for (; k < nx; ++k) {
-      const unsigned long long old = atomicAdd(&a.queue[die_at(k)], step_of(k));
-      w = claim_word_item(a.plan, die_at(k), old, k > 0);
+      const unsigned long long old = atomicAdd(&a.queue[die_at(k)], 1ull);
+      w = claim_word_item(a.plan, die_at(k), old);
       if (w >= 0) break;
     }
     used_up = k;
@@ -466,13 +464,13 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_fwd_pingpong(KernelArgs a) 
     int k = nx;
     if (threadIdx.x == 0) {
       k = used_up;
-      if (k < nx) ticket = atomicAdd(&a.queue[die_at(k)], step_of(k));
+      if (k < nx) ticket = atomicAdd(&a.queue[die_at(k)], 1ull);
     }
     attn_item_pingpong<D, T>(a, decode(a.plan, w), smem, [&]() __attribute__((always_inline)) {
       if (threadIdx.x == 0) {
         long long nw = -1;
         if (k < nx) {
-          nw = claim_word_item(a.plan, die_at(k), ticket, k > 0);
+          nw = claim_word_item(a.plan, die_at(k), ticket);
           if (nw < 0) nw = -2;
         }
         next_item = nw;

@@ -115,19 +115,17 @@ CA_HD int64_t plan_slot_work(const Plan& p, int64_t slot) {
 
 // Persistent launch: each die x owns the work of its launch slots
 // x, x + n_xcd, ... (count die_share_start(n, x+1) - die_share_start(n, x)) as
-// a queue.  A claim word packs the claims taken from the front (low 32 bits,
-// by the die's own workgroups, longest items first) and from the back (high 32
-// bits, by workgroups of dies whose own queue is empty).  `old` is the word's
-// value before this claim added 1 to its half; the claim gets the queue
-// position front or count-1-back while front + back < count, so every item is
-// taken exactly once, and -1 once the queue is used up.
-CA_HD int64_t claim_word_item(const Plan& p, int x, unsigned long long old, bool from_back) {
+// a queue, longest items first.  Its claim word counts the claims made on it,
+// by its own workgroups and, once theirs is used up, by other dies'.  `old` is
+// the word's value before this claim added 1: the claim gets queue position
+// old while old < count, so every item is taken exactly once, and -1 once the
+// queue is used up.  Taking stolen items from the front too keeps each die's
+// short items for the end of the launch, where they even out the finish.
+CA_HD int64_t claim_word_item(const Plan& p, int x, unsigned long long old) {
   const int64_t count = die_share_start(p.n_items, x + 1, p.n_xcd) -
                         die_share_start(p.n_items, x, p.n_xcd);
-  const int64_t front = (int64_t)(old & 0xFFFFFFFFull), back = (int64_t)(old >> 32);
-  if (front + back >= count) return -1;
-  const int64_t pos = from_back ? count - 1 - back : front;
-  return plan_slot_work(p, x + pos * p.n_xcd);
+  if ((int64_t)old >= count) return -1;
+  return plan_slot_work(p, x + (int64_t)old * p.n_xcd);
 }
 
 CA_HD Item decode(const Plan& p, int64_t w) {

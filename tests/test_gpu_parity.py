@@ -146,6 +146,35 @@ def test_work_queue_two_streams_interleaved():
         assert torch.equal(o, ref_a if i % 2 == 0 else ref_b), f"launch {i}"
 
 
+def test_work_queue_under_graph_replay():
+    """A queue step captured in a HIP graph and replayed several times, with
+    eager calls of the same context and synchronisations between replays: the
+    work queue's slot is fixed at capture, and the kernel zeroes it itself
+    (no memset node), so every replay gives the eager bits."""
+    ctx = ca.create(0, ca.FLAG_BLOCK256)
+    q, k, v = synth.queue_inputs(4, 600, 3, 128, seed=41, device=DEV)
+    ref = ca.queue_step(q, k, v, None, ctx=ctx)
+    torch.cuda.synchronize()
+    out = torch.empty_like(q)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up on the capture stream
+        ca.queue_step(q, k, v, None, out=out, ctx=ctx)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ca.queue_step(q, k, v, None, out=out, ctx=ctx)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep}"
+        eager = ca.queue_step(q, k, v, None, ctx=ctx)
+        torch.cuda.synchronize()
+        assert torch.equal(eager, ref), f"eager call after replay {rep}"
+
+
 def test_guard_bands_and_cache_slot0_never_read():
     n, L, H, D = 3, 150, 2, 128
     q, k, v = synth.queue_inputs(n, L, H, D, seed=8, device=DEV)

@@ -23,9 +23,11 @@
 //
 // Softmax: fixed reference maximum per row (the maximum of the row's first
 // key tile), as in attn_kernel.h; a work item whose l or O overflows writes the
-// overflow marker and is redone by chunk_attn_recheck.  The denominator l is
-// summed by the matrix core (see lacc), so a score pair costs the softmax wave
-// two FMAs, two exponentials and one pack.
+// overflow marker and is redone by chunk_attn_recheck.  A score pair costs the
+// softmax wave two FMAs, two exponentials, one pack and two adds into l.  (l
+// summed by the matrix core instead, with an all-ones operand, takes four of
+// the matrix phase's 36 MFMAs per tile, and the matrix phase is the longer
+// one: 2.6% slower.)
 //
 // The K/V tiles go global -> LDS by LDS DMA written as inline asm
 // (load_lds16_async): each wave waits for its own loads with vmcnt.
@@ -233,15 +235,10 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
   f32x16_t sacc[2];       // S^T of the current tile, two 32-key blocks
   uint32_t pk[2][8];      // P^T of the previous tile as bf16 pairs
   float m_run = 0.f;      // reference maximum (log2 domain)
-  // The softmax denominator l is summed by the matrix core: one extra MFMA
-  // per 16-key step with an all-ones A operand turns the P^T operand into its
-  // column sums (every row of the 32x32 result is l of the lane's query).  It
-  // sums the same bf16-rounded numerators the P.V product uses, and takes
-  // four vector instructions per score pair off the softmax phase.
-  f32x16_t lacc = f32x16_t{};
-  const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
-  const uint32_t one_w = __builtin_bit_cast(uint32_t, one2);
-  const u32x4_t ones = {one_w, one_w, one_w, one_w};
+  // The softmax denominator l: this lane's part (its 16 keys of each 32-key
+  // block), summed from the fp32 numerators in the softmax phase, one partial
+  // sum per key block; the two half-waves' parts are added in the epilogue.
+  float lsum0 = 0.f, lsum1 = 0.f;
   const float s2 = a.scale_log2;
 
   // Matrix phase of tile t: P.V of tile t-1 (kPV) and S of tile t (kQK), with
@@ -299,10 +296,6 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               __builtin_bit_cast(bf16x8_t, vf[i % 3]), __builtin_bit_cast(bf16x8_t, pb), oacc[db],
               0, 0, 0);
-          if (db == kDb - 1)
-            lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ones),
-                                                           __builtin_bit_cast(bf16x8_t, pb), lacc,
-                                                           0, 0, 0);
         }
       }
       // one step at a time: the scheduler would otherwise start most of the
@@ -338,6 +331,7 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
           if (key0 >= total) p0 = 0.f;
           if (key0 + 1 >= total) p1 = 0.f;
         }
+        if (kb2 == 0) lsum0 += p0 + p1; else lsum1 += p0 + p1;
         pk[kb2][i] = pack_bf16(p0, p1);
       }
   };
@@ -354,6 +348,7 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
   auto end_softmax = [&]() __attribute__((always_inline)) {
     pin(pk[0]);
     pin(pk[1]);
+    asm volatile("" : "+v"(lsum0), "+v"(lsum1));
     wg_barrier();
     pin(pk[0]);
     pin(pk[1]);
@@ -397,7 +392,8 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
 
   // ---- epilogue: overflow check over the workgroup (this barrier also joins
   // the two groups), then normalise and store this lane's query row
-  const float l_tot = lacc[0];
+  const float lh = lsum0 + lsum1;
+  const float l_tot = lh + other_half(lh);
   float acc = l_tot;
 #pragma unroll
   for (int db = 0; db < kDb; ++db)

@@ -226,13 +226,25 @@ def test_range_fingerprint_bit_exact(flags):
         assert torch.equal(out.cpu(), exp_bf16), "fingerprint mismatch"
 
 
-def test_constant_v_returned_exactly():
+@pytest.mark.parametrize("flags", FLAGS)
+def test_constant_v_returned(flags):
+    """Softmax weights sum to one, so a constant V row comes back.  The
+    128-row kernel sums l from the same bf16-rounded P the P.V product uses,
+    so its weights sum to one exactly and V comes back bit-exactly.  The
+    256-row kernel sums l from the fp32 numerators before rounding: its
+    weights sum to one within the rounding of P (relative 2^-9 per weight,
+    averaged over hundreds of keys), so V comes back within one bf16 step."""
     n, L, H, D = 3, 257, 2, 128
     q, k, _ = synth.queue_inputs(n, L, H, D, seed=10, device=DEV)
     cvec = synth.normal((1, 1, H, D), 10, 9, DEV)
     v = cvec.expand(n, L, H, D).contiguous()
-    out = run_queue(q, k, v)
-    assert torch.equal(out, v)
+    out = run_queue(q, k, v, flags=flags)
+    if flags == ca.FLAG_BLOCK128:
+        assert torch.equal(out, v)
+    else:
+        rel = ((out.float() - v.float()).abs() / v.float().abs()).max().item()
+        say("constant V, 256-row items: max relative difference", rel)
+        assert rel <= 2.0 ** -7
 
 
 def test_scale_zero_is_uniform_mean():
@@ -278,7 +290,7 @@ def test_device_plan_equals_host_plan(flags):
 def test_block_sizes_agree():
     """The two launch configurations run different schedules (128-row items:
     the synchronous one, l summed on the vector ALU; 256-row items: the
-    ping-pong one, l summed by the matrix core), so their sums round in a
+    ping-pong one, l summed from the unrounded numerators), so their sums round in a
     different order: they agree to a few bf16 rounding steps, well inside the
     parity bar each of them meets against the oracle."""
     q, k, v = synth.queue_inputs(5, 700, 3, 128, seed=14, device=DEV, k_rho=0.9)

@@ -49,6 +49,33 @@
 
 namespace chunkattn {
 
+// Two 1 KB LDS DMA chunks into consecutive LDS kilobytes, from one
+// wave-uniform base in scalar registers plus per-lane byte offsets: one M0
+// save and restore for both.  The first load waits as load_lds16_async does
+// (the base may have been written by a vector instruction just before); the
+// second needs only the one wait state an M0 write takes before an LDS DMA.
+__device__ __forceinline__ void load_lds16x2_async(const void* sbase, uint32_t voff0,
+                                                   uint32_t voff1, void* lds_chunk) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t m0 = (uint32_t)(uintptr_t)(CA_LDS void*)lds_chunk;
+  const uint64_t sb = (uint64_t)(uintptr_t)sbase;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 4\n\t"
+      "global_load_lds_dwordx4 %1, %3\n\t"
+      "s_add_i32 m0, m0, 0x400\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff0), "v"(voff1), "s"(sb), "s"(m0)
+      : "memory");
+#endif
+}
+
+
 // Eight 64-row tiles: K slots 0..3, then V slots 0..3.
 template <int D>
 constexpr uint32_t kPingPongLdsBytes = 8 * Geo<D>::kTileBytes;
@@ -117,6 +144,20 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
   vpre = uniform_ptr(vpre);
   kown = uniform_ptr(kown);
   vown = uniform_ptr(vown);
+  // Tiles wholly inside one segment: [0, np) in the predecessor, [no, nf) in
+  // the own chunk; the straddling tile and a ragged last tile take the
+  // per-row path.  Tile t's first row is at byte address base + t * tstride,
+  // with base the predecessor's start or, for own-chunk tiles, the own
+  // chunk's start minus pred rows (an integer, only ever offset forward into
+  // the own chunk).  Precomputed here, the per-tile address is one select and
+  // one multiply-add in scalar registers.
+  const int np = pred / kBN;
+  const int no = (pred + kBN - 1) / kBN;
+  const int nf = total / kBN;
+  const uint64_t tstride = (uint64_t)kBN * (uint64_t)rs * sizeof(T);
+  const uint64_t pshift = (uint64_t)pred * (uint64_t)rs * sizeof(T);
+  const uint64_t kpre_b = (uint64_t)(uintptr_t)kpre, vpre_b = (uint64_t)(uintptr_t)vpre;
+  const uint64_t kown_s = (uint64_t)(uintptr_t)kown - pshift, vown_s = (uint64_t)(uintptr_t)vown - pshift;
 
   // ---- Q fragment: B operand of S^T = K.Q^T, one query row per lane column
   const int qrow = it.q0 + wave * 32 + l32;
@@ -148,13 +189,18 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
     const T* own = kV ? vown : kown;
     const int r0 = t * kBN;
     if constexpr (sizeof(T) == 2) {
-      if (r0 + kBN <= pred || (r0 >= pred && r0 + kBN <= total)) {
-        const bool in_pred = r0 + kBN <= pred;
-        const char* base = reinterpret_cast<const char*>(
-            (in_pred ? pre : own) + (int64_t)(in_pred ? r0 : r0 - pred) * rs);
+      if (t < np || (t >= no && t < nf)) {
+        const uint64_t b = (t < np ? (kV ? vpre_b : kpre_b) : (kV ? vown_s : kown_s)) +
+                           (uint64_t)(uint32_t)t * tstride;
+        const char* base = reinterpret_cast<const char*>((uintptr_t)b);
+        if constexpr (kCpw == 2) {
+          load_lds16x2_async(base, kV ? voffs[0] : koffs[0], kV ? voffs[1] : koffs[1],
+                             dst + wave * kCpw * 1024);
+        } else {
 #pragma unroll
-        for (int i = 0; i < kCpw; ++i)
-          load_lds16_async(base, kV ? voffs[i] : koffs[i], dst + (wave * kCpw + i) * 1024);
+          for (int i = 0; i < kCpw; ++i)
+            load_lds16_async(base, kV ? voffs[i] : koffs[i], dst + (wave * kCpw + i) * 1024);
+        }
       } else {
         // straddling or ragged tile: rows past the end re-read the last row
 #pragma unroll

@@ -21,13 +21,18 @@
 // the two waves of a SIMD compete for instruction issue, and without it the
 // older wave's softmax slows the younger wave's matrix phase by a fifth.
 //
-// Softmax: fixed reference maximum per row (the maximum of the row's first
-// key tile), as in attn_kernel.h; a work item whose l or O overflows writes the
-// overflow marker and is redone by chunk_attn_recheck.  A score pair costs the
-// softmax wave two FMAs, two exponentials, one pack and two adds into l.  (l
-// summed by the matrix core instead, with an all-ones operand, takes four of
-// the matrix phase's 36 MFMAs per tile, and the matrix phase is the longer
-// one: 2.6% slower.)
+// Softmax without a maximum: Q is multiplied by scale * log2 e and rounded to
+// bf16 once per work item, so the matrix core returns the scores in the log2
+// domain and P = 2^S needs no subtraction.  softmax(S) is unchanged by leaving
+// the maximum out; only the range of fp32 is at stake, and a work item whose
+// l or O is not finite, or whose l is below 2^-64, writes the overflow marker
+// and is redone exactly by chunk_attn_recheck (running maximum).  A score pair
+// costs the softmax wave two exponentials, one pack and one dot2 into l, which
+// sums the rounded numerators: the weights of a row sum to one exactly, so a
+// row with one dominant key returns its value.  (l summed by the matrix core
+// instead, with an all-ones operand, takes four more MFMAs per tile from the
+// matrix phase; fp32 adds of the unrounded numerators leave a dominant key's
+// weight off by its bf16 rounding.)
 //
 // The K/V tiles go global -> LDS by LDS DMA written as inline asm
 // (load_lds16_async): each wave waits for its own loads with vmcnt.
@@ -167,6 +172,16 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
   for (int ks = 0; ks < kKs; ++ks)
     qf[ks] = qvalid ? Io<T>::load8(qb + (int64_t)qrow * rs + ks * 16 + hh * 8)
                     : u32x4_t{0u, 0u, 0u, 0u};
+  // scaled by scale * log2 e (nearest-even), so S^T comes out in the log2
+  // domain
+#pragma unroll
+  for (int ks = 0; ks < kKs; ++ks)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t x = qf[ks][w];
+      qf[ks][w] = pack_bf16(__uint_as_float(x << 16) * a.scale_log2,
+                            __uint_as_float(x & 0xffff0000u) * a.scale_log2);
+    }
 
   // ---- per-lane global load map: LDS chunk c = wave*kCpw + i of a tile
   // receives tile row c*kRowsPerKB + lane/kBlk, physical block lane%kBlk
@@ -280,43 +295,52 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
   for (int db = 0; db < kDb; ++db) oacc[db] = f32x16_t{};
   f32x16_t sacc[2];       // S^T of the current tile, two 32-key blocks
   uint32_t pk[2][8];      // P^T of the previous tile as bf16 pairs
-  float m_run = 0.f;      // reference maximum (log2 domain)
   // The softmax denominator l: this lane's part (its 16 keys of each 32-key
-  // block), summed from the fp32 numerators in the softmax phase, one partial
-  // sum per key block; the two half-waves' parts are added in the epilogue.
+  // block), summed in the softmax phase from the same bf16-rounded numerators
+  // the P.V product uses (one dot2 against (1, 1) per pair, two partial sums),
+  // so the weights sum to one exactly; the two half-waves' parts are added in
+  // the epilogue.
   float lsum0 = 0.f, lsum1 = 0.f;
-  const float s2 = a.scale_log2;
+  const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   // Matrix phase of tile t: P.V of tile t-1 (kPV) and S of tile t (kQK), with
   // K(t) at LDS byte offset k_at and V(t-1) at v_at.  The two MFMA streams
-  // are interleaved step by step; the LDS reads run two steps ahead.
-  auto matrix_phase = [&](uint32_t k_at, uint32_t v_at, auto pv_tag, auto qk_tag)
+  // are interleaved step by step; the LDS reads run two steps ahead.  With
+  // kPf the first two steps' fragments are already in kf/vf (read at the end
+  // of the softmax phase before).
+  // LDS fragment reads.  QK step i: key block i / kKs, k-step i % kKs (key
+  // block 0 first, so the first two steps read only key rows 0-31); PV step
+  // i: 16-key step i / kDb, d-block i % kDb.
+  auto rk = [&](uint32_t k_at, int i) __attribute__((always_inline)) {
+    const CA_LDS unsigned char* kl = (const CA_LDS unsigned char*)smem + k_at;
+    return *(CA_LDS const u32x4_t*)(kl + koff_lds[i % kKs] + (i / kKs) * 32 * G::kRowBytes);
+  };
+  auto rv = [&](uint32_t v_at, int i) __attribute__((always_inline)) {
+    const CA_LDS unsigned char* vl = (const CA_LDS unsigned char*)smem + v_at;
+    const int db = i % kDb;
+    const uint32_t imm = 16 * (i / kDb) * G::kRowBytes;
+    const i16x4_t lo =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((CA_LDS i16x4_t*)(vl + voff_lds[db][0] + imm));
+    const i16x4_t hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((CA_LDS i16x4_t*)(vl + voff_lds[db][1] + imm));
+    const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
+    const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
+    return u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
+  };
+  u32x4_t kf[3], vf[3];  // K and V fragments in flight (ring of three steps)
+  auto matrix_phase = [&](uint32_t k_at, uint32_t v_at, auto pv_tag, auto qk_tag, auto pf_tag)
       __attribute__((always_inline)) {
     constexpr bool kPV = decltype(pv_tag)::value;
     constexpr bool kQK = decltype(qk_tag)::value;
-    const CA_LDS unsigned char* kl = (const CA_LDS unsigned char*)smem + k_at;
-    const CA_LDS unsigned char* vl = (const CA_LDS unsigned char*)smem + v_at;
-    // QK step i: key block i & 1, k-step i >> 1; PV step i: 16-key step
-    // i / kDb, d-block i % kDb
-    auto read_k = [&](int i) __attribute__((always_inline)) {
-      return *(CA_LDS const u32x4_t*)(kl + koff_lds[i >> 1] + (i & 1) * 32 * G::kRowBytes);
-    };
-    auto read_v = [&](int i) __attribute__((always_inline)) {
-      const int db = i % kDb;
-      const uint32_t imm = 16 * (i / kDb) * G::kRowBytes;
-      const i16x4_t lo =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((CA_LDS i16x4_t*)(vl + voff_lds[db][0] + imm));
-      const i16x4_t hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((CA_LDS i16x4_t*)(vl + voff_lds[db][1] + imm));
-      const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
-      const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
-      return u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
-    };
-    u32x4_t kf[3], vf[3];
+    constexpr bool kPf = decltype(pf_tag)::value;
+    auto read_k = [&](int i) __attribute__((always_inline)) { return rk(k_at, i); };
+    auto read_v = [&](int i) __attribute__((always_inline)) { return rv(v_at, i); };
+    if constexpr (!kPf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      if constexpr (kQK) kf[i] = read_k(i);
-      if constexpr (kPV) vf[i] = read_v(i);
+      for (int i = 0; i < 2; ++i) {
+        if constexpr (kQK) kf[i] = read_k(i);
+        if constexpr (kPV) vf[i] = read_v(i);
+      }
     }
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
@@ -328,7 +352,7 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
       }
       if constexpr (kQK) {
         if (i < kStepsQK) {
-          const int kb2 = i & 1, ks = i >> 1;
+          const int kb2 = i / kKs, ks = i % kKs;
           sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               __builtin_bit_cast(bf16x8_t, kf[i % 3]), __builtin_bit_cast(bf16x8_t, qf[ks]),
               ks == 0 ? f32x16_t{} : sacc[kb2], 0, 0, 0);
@@ -350,35 +374,28 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
     }
   };
 
-  // Softmax phase of tile t: numerators of the scores in sacc into pk and l
-  // (with kFirst, the reference maximum first; with a mask, keys >= total get
-  // P = 0).  Keys past the end of a ragged tile re-read the last key row, so
-  // they repeat an existing score and never raise the maximum.
-  auto softmax_phase = [&](int t, auto first_tag, auto mask_tag) __attribute__((always_inline)) {
-    if constexpr (decltype(first_tag)::value) {
-      float t8[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int kb2 = i >> 2, j = (i & 3) * 4;
-        t8[i] = fmaxf(fmaxf(sacc[kb2][j], sacc[kb2][j + 1]), fmaxf(sacc[kb2][j + 2], sacc[kb2][j + 3]));
-      }
-      const float mx = fmaxf(fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3])),
-                             fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7])));
-      m_run = fmaxf(mx, other_half(mx)) * s2;
-    }
+  // Softmax phase of tile t: numerators 2^S of the scores in sacc into pk and
+  // l (with a mask, keys >= total get P = 0; they re-read the last key row,
+  // so their scores are finite).
+  auto softmax_phase = [&](int t, auto mask_tag) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][2 * i], s2, -m_run));
-        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb2][2 * i + 1], s2, -m_run));
+        float p0 = __builtin_amdgcn_exp2f(sacc[kb2][2 * i]);
+        float p1 = __builtin_amdgcn_exp2f(sacc[kb2][2 * i + 1]);
         if constexpr (decltype(mask_tag)::value) {
           const int key0 = t * kBN + kb2 * 32 + 8 * ((2 * i) >> 2) + 4 * hh + ((2 * i) & 3);
           if (key0 >= total) p0 = 0.f;
           if (key0 + 1 >= total) p1 = 0.f;
         }
-        if (kb2 == 0) lsum0 += p0 + p1; else lsum1 += p0 + p1;
-        pk[kb2][i] = pack_bf16(p0, p1);
+        const uint32_t w = pack_bf16(p0, p1);
+        pk[kb2][i] = w;
+        const bf16x2_t pw = __builtin_bit_cast(bf16x2_t, w);
+        if ((i & 1) == 0)
+          lsum0 = __builtin_amdgcn_fdot2_f32_bf16(pw, one2, lsum0, false);
+        else
+          lsum1 = __builtin_amdgcn_fdot2_f32_bf16(pw, one2, lsum1, false);
       }
   };
 
@@ -407,12 +424,24 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
     // the matrix phase issues at the higher wave priority, so the SIMD picks
     // this wave's MFMAs and LDS reads over the other wave's softmax
     __builtin_amdgcn_s_setprio(3);
-    matrix_phase(kslot(t), vslot(t - 1), std::integral_constant<bool, !kFirst>{}, std::true_type{});
+    matrix_phase(kslot(t), vslot(t - 1), std::integral_constant<bool, !kFirst>{}, std::true_type{},
+                 std::integral_constant<bool, !kFirst>{});
     __builtin_amdgcn_s_setprio(0);
     wait_left(group_loads(t + 2));
     end_matrix();
-    softmax_phase(t, first_tag, mask_tag);
+    softmax_phase(t, mask_tag);
     issue(t + 3);
+    // The next matrix phase's first two steps: key rows 0-31 of K(t+1) and
+    // rows 0-15 of V(t).  Waves 0-3 load rows 0-31 of every tile; they waited
+    // for these loads at the end of their matrix phase of tile t, and the
+    // barrier after it made them visible, before either group gets here.  The
+    // read latency moves into the softmax phase.
+    if (t + 1 < n_tiles) {
+      kf[0] = rk(kslot(t + 1), 0);
+      kf[1] = rk(kslot(t + 1), 1);
+    }
+    vf[0] = rv(vslot(t), 0);
+    vf[1] = rv(vslot(t), 1);
     end_softmax();
   };
 
@@ -433,11 +462,11 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
     for (int t = 1; t + 1 < n_tiles; ++t) step(t, std::false_type{}, NoMask{});
     step(n_tiles - 1, std::false_type{}, Mask{});
   }
-  matrix_phase(0u, vslot(n_tiles - 1), std::true_type{}, std::false_type{});
+  matrix_phase(0u, vslot(n_tiles - 1), std::true_type{}, std::false_type{}, std::true_type{});
   if (!group_b) wg_barrier();  // matches group B's first barrier
 
-  // ---- epilogue: overflow check over the workgroup (this barrier also joins
-  // the two groups), then normalise and store this lane's query row
+  // ---- epilogue: range check over the workgroup (this barrier also joins the
+  // two groups), then normalise and store this lane's query row
   const float lh = lsum0 + lsum1;
   const float l_tot = lh + other_half(lh);
   float acc = l_tot;
@@ -446,7 +475,7 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc += oacc[db][i];
   T* ob = static_cast<T*>(a.o) + e * a.o_bstride + (int64_t)it.h * D;
-  if (__syncthreads_or(!__builtin_isfinite(acc))) {
+  if (__syncthreads_or(!__builtin_isfinite(acc) || !(l_tot >= 0x1p-64f))) {
     if (tid == 0) ob[(int64_t)it.q0 * rs] = overflow_marker<T>();
     return;
   }

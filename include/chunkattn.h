@@ -31,11 +31,10 @@
  *                  predecessor's K (index 0) then V (index 1); slot 0 is never read.
  *
  * Numerics.  Q.K^T and P.V run on bf16 matrix cores with fp32 accumulation and
- * an fp32 online softmax; P is rounded to bf16 before the P.V product.  The
- * softmax denominator is summed from the same rounded P with 128-row work items
- * (so a constant V comes back bit-exactly) and from the fp32 numerators before
- * rounding with 256-row items (a constant V comes back within one bf16
- * rounding step).  dtype F32 means fp32
+ * an fp32 softmax; P is rounded to bf16 before the P.V product and the
+ * softmax denominator is summed from the same rounded P, so a constant V comes
+ * back bit-exactly.  With 256-row work items Q is multiplied by scale * log2 e
+ * and rounded to bf16 once per item (relative 2^-9 per element).  dtype F32 means fp32
  * storage in and out, rounded to bf16 (nearest-even) on load.  bf16 outputs are
  * rounded nearest-even.  Results are bitwise deterministic run to run, and the
  * separate-cache and in-place-predecessor forms give bitwise-equal outputs.

@@ -264,8 +264,9 @@ struct Mask {
   static constexpr bool value = true;
 };
 
-// Marks a work item whose fixed-maximum pass overflowed: a quiet NaN in the
-// first element of its first query row (the output of finite inputs is finite).
+// Marks a work item whose main pass left fp32's range (either kernel's): a
+// quiet NaN in the first element of its first query row (the output of finite
+// inputs is finite).
 template <typename T>
 __device__ __forceinline__ T overflow_marker() {
   return __builtin_bit_cast(T, std::conditional_t<sizeof(T) == 2, uint16_t, uint32_t>(

@@ -212,9 +212,10 @@ hipError_t allow_pingpong_lds() {
   return e;
 }
 
-// The fixed-maximum pass (W = 8: 256-row work items on the ping-pong
-// schedule; W = 4: 128-row items on the synchronous one), then the overflow
-// recheck (synchronous schedule, running maximum) on the same stream.
+// The main pass (W = 8: 256-row work items on the ping-pong schedule, softmax
+// without a maximum; W = 4: 128-row items on the synchronous one, fixed
+// maximum), then the range recheck (synchronous schedule, running maximum) on
+// the same stream.
 // W = 8: the main pass is persistent, n_persist workgroups (one per CU) share
 // the work items through the work queue a.queue.
 template <int D, typename T, int W>

@@ -438,3 +438,26 @@ def test_score_overflow_falls_back_exactly(flags):
     # chunk 1 averages V over its 50 high-scoring own rows
     exp1 = v[1, 150:].float().mean(0)
     torch.testing.assert_close(out[1].float(), exp1.expand(L, H, D), atol=1e-2, rtol=0)
+
+
+@pytest.mark.parametrize("flags", FLAGS)
+def test_score_underflow_falls_back_exactly(flags):
+    """Every score of a row far below zero (-226 / ln 2 in the exponent) sends
+    the sum of weights out of fp32's range at the low end for a softmax
+    without a maximum (the 256-row kernel marks l < 2^-64); the result must
+    still be the exact softmax.  Chunk 1's last 50 own keys score 1/128 of
+    the others' magnitude less negative, so they take almost all the weight;
+    chunk 0's keys all score the same, so it returns the mean of its V."""
+    n, L, H, D = 2, 200, 2, 128
+    q = torch.full((n, L, H, D), -20.0, dtype=torch.bfloat16, device=DEV)
+    k = torch.ones((n, L, H, D), dtype=torch.bfloat16, device=DEV)
+    k[1, 150:] = 0.5            # score -113 instead of -226 for these keys
+    v = synth.normal((n, L, H, D), 16, 3, DEV)
+    cache = synth.build_cache(k, v)
+    out = run_queue(q, k, v, cache, flags=flags)
+    ref = oracle.queue_step(q, k, v, cache)
+    assert_parity(to_f64(out), ref, "underflow fallback")
+    exp0 = v[0].float().mean(0)
+    torch.testing.assert_close(out[0].float(), exp0.expand(L, H, D), atol=1e-2, rtol=0)
+    exp1 = v[1, 150:].float().mean(0)
+    torch.testing.assert_close(out[1].float(), exp1.expand(L, H, D), atol=1e-2, rtol=0)

@@ -297,10 +297,11 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
   uint32_t pk[2][8];      // P^T of the previous tile as bf16 pairs
   // The softmax denominator l: this lane's part (its 16 keys of each 32-key
   // block), summed in the softmax phase from the same bf16-rounded numerators
-  // the P.V product uses (one dot2 against (1, 1) per pair, two partial sums),
-  // so the weights sum to one exactly; the two half-waves' parts are added in
-  // the epilogue.
-  float lsum0 = 0.f, lsum1 = 0.f;
+  // the P.V product uses (one dot2 against (1, 1) per pair), so the weights sum
+  // to one exactly; the two half-waves' parts are added in the epilogue.  Eight
+  // partial sums keep each dot2's accumulator chain two deep (with two, the
+  // chains' latency held up the softmax phase: 1.6% slower overall).
+  float lsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   // Matrix phase of tile t: P.V of tile t-1 (kPV) and S of tile t (kQK), with
@@ -392,10 +393,8 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
         const uint32_t w = pack_bf16(p0, p1);
         pk[kb2][i] = w;
         const bf16x2_t pw = __builtin_bit_cast(bf16x2_t, w);
-        if ((i & 1) == 0)
-          lsum0 = __builtin_amdgcn_fdot2_f32_bf16(pw, one2, lsum0, false);
-        else
-          lsum1 = __builtin_amdgcn_fdot2_f32_bf16(pw, one2, lsum1, false);
+        const int li = (i & 3) + 4 * kb2;
+        lsum[li] = __builtin_amdgcn_fdot2_f32_bf16(pw, one2, lsum[li], false);
       }
   };
 
@@ -411,7 +410,8 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
   auto end_softmax = [&]() __attribute__((always_inline)) {
     pin(pk[0]);
     pin(pk[1]);
-    asm volatile("" : "+v"(lsum0), "+v"(lsum1));
+    asm volatile("" : "+v"(lsum[0]), "+v"(lsum[1]), "+v"(lsum[2]), "+v"(lsum[3]));
+    asm volatile("" : "+v"(lsum[4]), "+v"(lsum[5]), "+v"(lsum[6]), "+v"(lsum[7]));
     wg_barrier();
     pin(pk[0]);
     pin(pk[1]);
@@ -467,7 +467,7 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
 
   // ---- epilogue: range check over the workgroup (this barrier also joins the
   // two groups), then normalise and store this lane's query row
-  const float lh = lsum0 + lsum1;
+  const float lh = ((lsum[0] + lsum[1]) + (lsum[2] + lsum[3])) + ((lsum[4] + lsum[5]) + (lsum[6] + lsum[7]));
   const float l_tot = lh + other_half(lh);
   float acc = l_tot;
 #pragma unroll

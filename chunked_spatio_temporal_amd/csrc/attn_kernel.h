@@ -88,9 +88,8 @@ struct KernelArgs {
   int ring_tail;
   // Work queue of the persistent 256-row main pass (chunk_attn_fwd_pingpong;
   // the other kernels take item plan_slot_work(blockIdx.x)).  Word x <
-  // n_xcd counts the claims on die x's share (claim_word_item), word n_xcd the
-  // finished workgroups; all zero at launch, and the last workgroup to finish
-  // zeroes them again.
+  // n_xcd counts the claims on die x's share (claim_word_item); queue_clear
+  // zeroes the words on the same stream just before the launch.
   unsigned long long* queue;
 
   // Physical entry of batch index b (b > -ring_slots).
@@ -637,6 +636,15 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_recheck(KernelArgs a
                                               (int64_t)it.h * D];
   if (!__builtin_isnan((float)first)) return;
   attn_item_sync<D, T, W, false>(a, it, smem);
+}
+
+// Zeroes the n claim words of a work queue (one thread per word), launched on
+// the stream of the persistent main pass just before it.  A kernel rather than
+// a memset, so that it can sit in a captured graph and repeats on every
+// replay; and because every launch starts from cleared words, no earlier
+// launch has to leave them clean.
+__global__ void queue_clear(unsigned long long* words, int n) {
+  if ((int)threadIdx.x < n) words[threadIdx.x] = 0ull;
 }
 
 // Writes the decoded work item of every workgroup slot (7 ints each), using

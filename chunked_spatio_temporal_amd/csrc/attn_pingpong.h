@@ -500,7 +500,8 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
 // ends up with less work and a new item needs no workgroup launch.  Thread 0
 // starts the claim of the next item before the current one; the atomic's
 // latency overlaps the first tile's load, whose wait (vmcnt 0) also covers it,
-// and the result goes to LDS after the prologue's barrier.
+// and the result goes to LDS after the prologue's barrier.  The claim words
+// (a.queue[0 .. n_xcd)) are zero at launch (queue_clear runs just before).
 template <int D, typename T>
 __global__ __launch_bounds__(512, 1) void chunk_attn_fwd_pingpong(KernelArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
@@ -558,12 +559,6 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_fwd_pingpong(KernelArgs a) 
       wg_barrier();
       w = next_item;
     }
-  }
-  // the last workgroup to finish leaves the queue zeroed for the next launch
-  if (threadIdx.x == 0) {
-    const unsigned long long done = atomicAdd(&a.queue[nx], 1ull);
-    if (done == (unsigned long long)gridDim.x - 1)
-      for (int x = 0; x <= nx; ++x) atomicExch(&a.queue[x], 0ull);
   }
 }
 

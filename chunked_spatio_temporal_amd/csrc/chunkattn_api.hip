@@ -17,11 +17,16 @@
 #include "fifo.h"
 #include "noise.h"
 
-// Work-queue slots of a context: each call of the persistent (256-row) main
-// pass takes the next slot, so up to kQueueSlots calls may be in flight on
-// different streams at once.  A slot is kQueueWords 64-bit words (one claim
-// word per die, one finished-workgroup counter), zero between launches.
+// Work-queue slots of a context.  A slot is kQueueWords 64-bit words (one
+// claim word per die), cleared by a kernel on the call's stream right before
+// the persistent (256-row) main pass that uses it.  Eager calls take the next
+// of kQueueSlots slots in turn, so up to kQueueSlots of them may be in flight
+// on different streams at once.  A call made while its stream is being
+// captured into a graph takes a slot of its own from the next kCaptureSlots,
+// never used again by another call of the context: the graph keeps that slot
+// for all its replays, and eager calls or other graphs cannot land on it.
 constexpr int kQueueSlots = 64;
+constexpr int kCaptureSlots = 448;
 constexpr int kQueueWords = 16;
 
 struct chunkattn_ctx {
@@ -29,8 +34,10 @@ struct chunkattn_ctx {
   int n_cu = 0;
   int n_xcd = 1;
   int waves = 8;  // waves per workgroup; a work item covers 32 * waves query rows
-  unsigned long long* queue = nullptr;  // device, kQueueSlots * kQueueWords words
+  // device, (kQueueSlots + kCaptureSlots) * kQueueWords words
+  unsigned long long* queue = nullptr;
   std::atomic<unsigned> next_slot{0};
+  std::atomic<unsigned> next_capture{0};
   std::string arch;
   std::string err;
 };
@@ -81,6 +88,14 @@ int check_common(std::string* err, int heads, int head_dim, float scale, int dty
 // inside int64 and every row index of the kernel inside int32.
 constexpr long double kMaxElems = 4.0e18L;
 
+// The kernels address the rows of one 64-row key/value tile by 32-bit
+// per-lane byte offsets from the tile's first row (up to 63 rows of
+// heads * head_dim elements, plus the row itself): they must stay below 2^32.
+bool tile_offsets_fit(int heads, int head_dim, int dtype) {
+  const long double span = 64.0L * heads * head_dim * elem_size(dtype);
+  return span < 4294967296.0L;
+}
+
 // Queue step (window = false) and window step (window = true: out holds two
 // chunks' rows per window, a work item walks up to 3 * chunk_len key rows).
 int validate_queue(std::string* err, const void* q, const void* k, const void* v,
@@ -99,6 +114,9 @@ int validate_queue(std::string* err, const void* q, const void* k, const void* v
     return set_err(err, CHUNKATTN_EINVAL, "tensor size overflows 64-bit offsets");
   if ((long double)heads * head_dim > 2147483647.0L)
     return set_err(err, CHUNKATTN_EINVAL, "heads * head_dim overflows int32");
+  if (!tile_offsets_fit(heads, head_dim, dtype))
+    return set_err(err, CHUNKATTN_EUNSUPPORTED,
+                   "heads * head_dim too large: a 64-row key/value tile must span under 4 GiB");
   if (!q || !k || !v || !out)
     return set_err(err, CHUNKATTN_EINVAL, "q, k, v and out must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
@@ -154,6 +172,9 @@ int validate_full(std::string* err, const void* q, const void* k, const void* v,
     return set_err(err, CHUNKATTN_EINVAL, "tensor size overflows 64-bit offsets");
   if (row > 2147483647.0L)
     return set_err(err, CHUNKATTN_EINVAL, "heads * head_dim overflows int32");
+  if (!tile_offsets_fit(heads, head_dim, dtype))
+    return set_err(err, CHUNKATTN_EUNSUPPORTED,
+                   "heads * head_dim too large: a 64-row key/value tile must span under 4 GiB");
   if (!q || !k || !v || !out)
     return set_err(err, CHUNKATTN_EINVAL, "q, k, v and out must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
@@ -223,9 +244,13 @@ hipError_t launch_t(const KernelArgs& a, int n_persist, hipStream_t stream) {
   const dim3 grid((unsigned)a.plan.n_items);
   constexpr uint32_t kLds = chunkattn::kSyncLdsBytes<D>;
   if constexpr (W == 8) {
-    if (!a.queue || n_persist < 1) return hipErrorInvalidValue;
+    if (!a.queue || n_persist < 1 || a.plan.n_xcd > kQueueWords) return hipErrorInvalidValue;
     const hipError_t el = allow_pingpong_lds<D, T>();
     if (el != hipSuccess) return el;
+    hipLaunchKernelGGL(chunkattn::queue_clear, dim3(1), dim3(64), 0, stream, a.queue,
+                       a.plan.n_xcd);
+    const hipError_t ec = hipGetLastError();
+    if (ec != hipSuccess) return ec;
     hipLaunchKernelGGL((chunkattn::chunk_attn_fwd_pingpong<D, T>), dim3((unsigned)n_persist),
                        dim3(512),
                        chunkattn::kPingPongLdsBytes<D>, stream, a);
@@ -277,9 +302,23 @@ int run(chunkattn_ctx* ctx, const KernelArgs& args, int head_dim, int dtype, voi
   KernelArgs a = args;
   a.queue = nullptr;
   if (ctx->waves == 8) {
-    // one claim word per die and the finished count must fit in a slot
-    if (a.plan.n_xcd >= kQueueWords) a.plan.n_xcd = 1;
-    const unsigned slot = ctx->next_slot.fetch_add(1, std::memory_order_relaxed) % kQueueSlots;
+    // one claim word per die must fit in a slot
+    if (a.plan.n_xcd > kQueueWords) a.plan.n_xcd = 1;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap) != hipSuccess)
+      return set_err(&ctx->err, CHUNKATTN_ELAUNCH, "cannot query the stream's capture state");
+    unsigned slot;
+    if (cap == hipStreamCaptureStatusActive) {
+      const unsigned c = ctx->next_capture.fetch_add(1, std::memory_order_relaxed);
+      if (c >= (unsigned)kCaptureSlots) {
+        ctx->next_capture.store(kCaptureSlots, std::memory_order_relaxed);
+        return set_err(&ctx->err, CHUNKATTN_EUNSUPPORTED,
+                       "more than %d calls captured into graphs on one context", kCaptureSlots);
+      }
+      slot = kQueueSlots + c;
+    } else {
+      slot = ctx->next_slot.fetch_add(1, std::memory_order_relaxed) % kQueueSlots;
+    }
     a.queue = ctx->queue + (size_t)slot * kQueueWords;
   }
   const int n_persist = (int)(a.plan.n_items < ctx->n_cu ? a.plan.n_items : ctx->n_cu);
@@ -337,9 +376,10 @@ int chunkattn_create(chunkattn_ctx** out, int device_ordinal, unsigned flags) {
       xcc > 0)
     ctx->n_xcd = xcc;
   if (ctx->waves == 8) {
-    // the work queue of the persistent main pass, zeroed once here
+    // the work queues of the persistent main pass (each launch clears its own)
     DeviceGuard g(device_ordinal);
-    const size_t bytes = sizeof(unsigned long long) * kQueueSlots * kQueueWords;
+    const size_t bytes =
+        sizeof(unsigned long long) * (kQueueSlots + kCaptureSlots) * kQueueWords;
     void* q = nullptr;
     if (!g.ok || hipMalloc(&q, bytes) != hipSuccess) {
       delete ctx;

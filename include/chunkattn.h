@@ -41,16 +41,26 @@
  *
  * Ownership and asynchrony.  Every tensor pointer is device memory owned by the
  * caller and must stay valid until the stream work completes.  The library
- * owns only the context; a context of 256-row work items also owns an 8 KB
- * device buffer, the work queue of its persistent main pass, allocated and
- * zeroed by chunkattn_create.  queue_step and full make no allocation: they
+ * owns only the context; a context of 256-row work items also owns a 64 KB
+ * device buffer, 512 work-queue slots of its persistent main pass, allocated
+ * by chunkattn_create.  queue_step and full make no allocation: they
  * validate, enqueue the kernels on hip_stream (NULL = the legacy default
  * stream) and return; a device fault surfaces at the caller's next
  * synchronisation.  One context may be used by one host thread at a time;
- * separate contexts are independent.  Each call of a 256-row context takes
- * the next of 64 work-queue slots, which its last workgroup leaves zeroed:
- * calls may be spread over several streams as long as at most 64 of them are
- * in flight at once (calls on one stream never overlap).
+ * separate contexts are independent.  Each call of a 256-row context uses one
+ * work-queue slot, which a small kernel on hip_stream clears right before the
+ * main pass.  Eager calls take the next of 64 slots in turn: calls may be
+ * spread over several streams as long as at most 64 of them are in flight at
+ * once (calls on one stream never overlap).  A call made while hip_stream is
+ * being captured into a graph gets a slot of its own (at most 448 such calls
+ * per context; the next one fails with CHUNKATTN_EUNSUPPORTED), which only
+ * that graph's replays use: replays of different graphs may overlap each
+ * other and eager calls; replays of one graph must not overlap each other
+ * (launches of one executable graph are ordered).
+ *
+ * Sizes.  heads * head_dim * element size * 64 must stay below 2^32 (the
+ * kernels address a 64-row key/value tile by 32-bit byte offsets); larger
+ * rows fail with CHUNKATTN_EUNSUPPORTED.
  *
  * Errors.  Every call returns a chunkattn_status synchronously, before any
  * launch, for bad arguments; chunkattn_last_error() then holds a one-line

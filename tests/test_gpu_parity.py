@@ -40,8 +40,15 @@ def say(*a):
 FLAGS = [pytest.param(ca.FLAG_BLOCK256, id="bm256"), pytest.param(ca.FLAG_BLOCK128, id="bm128")]
 
 
+# Finite prefill of outputs that must be overwritten everywhere: above every
+# output of finite inputs here, and not NaN (the recheck pass recomputes items
+# whose first element is NaN, so a NaN prefill would hide a skipped item).
+UNWRITTEN = 2.0 ** 100
+
+
 def run_queue(q, k, v, cache=None, scale=None, flags=0):
-    out = ca.queue_step(q, k, v, cache, scale=scale, ctx=ca.create(0, flags))
+    out = torch.full_like(q, UNWRITTEN)
+    ca.queue_step(q, k, v, cache, out=out, scale=scale, ctx=ca.create(0, flags))
     torch.cuda.synchronize()
     return out
 
@@ -102,9 +109,10 @@ def test_deterministic_and_order_independent_of_stream_state():
 
 def test_work_queue_slots_reused_across_many_calls():
     """The 256-row main pass is persistent and takes its items from a work
-    queue that the last workgroup zeroes again; a context cycles through 64
-    queue slots.  150 back-to-back calls (every slot used twice or more), each
-    into a NaN-filled output, all give the first call's bits: no item is
+    queue slot that a clearing kernel zeroes right before it; eager calls cycle
+    through 64 slots.  150 back-to-back calls (every slot used twice or more),
+    each into an output prefilled with a finite sentinel (NaN would be
+    recomputed by the recheck pass), all give the first call's bits: no item is
     skipped or done twice after a slot is reused."""
     ctx = ca.create(0, ca.FLAG_BLOCK256)
     inputs = [synth.queue_inputs(4, 200, 3, 128, seed=s, device=DEV) for s in (21, 22)]
@@ -115,7 +123,7 @@ def test_work_queue_slots_reused_across_many_calls():
     outs = []
     for i in range(150):
         q, k, v = inputs[i % 2]
-        o = torch.full_like(q, float("nan"))
+        o = torch.full_like(q, 2.0 ** 100)
         ca.queue_step(q, k, v, None, out=o, ctx=ctx)
         outs.append(o)
     torch.cuda.synchronize()
@@ -138,7 +146,7 @@ def test_work_queue_two_streams_interleaved():
     for i in range(6):
         for st, inp in ((s1, a_in), (s2, b_in)):
             with torch.cuda.stream(st):
-                o = torch.full_like(inp[0], float("nan"))
+                o = torch.full_like(inp[0], 2.0 ** 100)
                 ca.queue_step(*inp, None, out=o, ctx=ctx, stream=st)
             outs.append(o)
     torch.cuda.synchronize()
@@ -149,8 +157,8 @@ def test_work_queue_two_streams_interleaved():
 def test_work_queue_under_graph_replay():
     """A queue step captured in a HIP graph and replayed several times, with
     eager calls of the same context and synchronisations between replays: the
-    work queue's slot is fixed at capture, and the kernel zeroes it itself
-    (no memset node), so every replay gives the eager bits."""
+    captured call has a work-queue slot of its own, cleared by a kernel node
+    (no memset node) on every replay, so every replay gives the eager bits."""
     ctx = ca.create(0, ca.FLAG_BLOCK256)
     q, k, v = synth.queue_inputs(4, 600, 3, 128, seed=41, device=DEV)
     ref = ca.queue_step(q, k, v, None, ctx=ctx)
@@ -166,13 +174,54 @@ def test_work_queue_under_graph_replay():
     with torch.cuda.graph(g):
         ca.queue_step(q, k, v, None, out=out, ctx=ctx)
     for rep in range(4):
-        out.fill_(float("nan"))
+        out.fill_(2.0 ** 100)
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {rep}"
         eager = ca.queue_step(q, k, v, None, ctx=ctx)
         torch.cuda.synchronize()
         assert torch.equal(eager, ref), f"eager call after replay {rep}"
+
+
+def test_two_graphs_on_two_streams_with_eager_calls():
+    """Two queue steps captured into two graphs, replayed at the same time on
+    two streams while eager calls of the same context run on a third, for 70
+    rounds (the eager calls wrap round all 64 eager slots): captured calls own
+    their slots, so no two launches in flight share one, and every output
+    equals its eager reference bit for bit."""
+    ctx = ca.create(0, ca.FLAG_BLOCK256)
+    ins = [synth.queue_inputs(4, 600, 3, 128, seed=s, device=DEV) for s in (51, 52, 53)]
+    refs = [ca.queue_step(*x, None, ctx=ctx) for x in ins]
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(x[0]) for x in ins[:2]]
+    graphs = []
+    for i in range(2):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):  # warm-up on a side stream
+            ca.queue_step(*ins[i], None, out=outs[i], ctx=ctx)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            ca.queue_step(*ins[i], None, out=outs[i], ctx=ctx)
+        graphs.append(g)
+    s1, s2, s3 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    eager = torch.empty_like(ins[2][0])
+    for rep in range(70):
+        for o in outs + [eager]:
+            o.fill_(2.0 ** 100)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            graphs[0].replay()
+        with torch.cuda.stream(s2):
+            graphs[1].replay()
+        with torch.cuda.stream(s3):
+            ca.queue_step(*ins[2], None, out=eager, ctx=ctx, stream=s3)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], refs[0]), f"graph 0, round {rep}"
+        assert torch.equal(outs[1], refs[1]), f"graph 1, round {rep}"
+        assert torch.equal(eager, refs[2]), f"eager call, round {rep}"
 
 
 def test_guard_bands_and_cache_slot0_never_read():
@@ -358,7 +407,9 @@ def gather_rows(out, rows):
 
 
 def check_any_size_properties(out, v):
-    """Outputs are convex combinations of V rows: finite and within V's range."""
+    """Outputs are convex combinations of V rows: finite and within V's range.
+    Outputs are prefilled with UNWRITTEN, so this also shows that every
+    element was written."""
     assert torch.isfinite(out).all()
     vmax = v.float().abs().amax().item()
     assert out.float().abs().amax().item() <= vmax * (1 + 2 ** -7)
@@ -387,7 +438,8 @@ def test_queue_workload_sampled_parity(name):
     if w.n_text:
         qx = synth.cross_queries(w.n, w.L, w.H, w.D, w.seed, DEV)
         kt, vt = synth.text_inputs(w.n_text, w.H, w.D, w.seed, DEV)
-        ox = ca.full(qx, kt, vt, scale=w.scale)
+        ox = torch.full_like(qx, UNWRITTEN)
+        ca.full(qx, kt, vt, out=ox, scale=w.scale)
         torch.cuda.synchronize()
         check_any_size_properties(ox, vt)
         xrows = sample_rows(w.n, w.L, w.H, rng, per=8)
@@ -411,7 +463,8 @@ def test_full_sequence_workload_sampled_parity():
     q = synth.normal((1, w.L, w.H, w.D), w.seed, synth.Q_ID, DEV)
     k = synth.normal((1, w.lkv, w.H, w.D), w.seed, synth.K_ID, DEV)
     v = synth.normal((1, w.lkv, w.H, w.D), w.seed, synth.V_ID, DEV)
-    out = ca.full(q, k, v, scale=w.scale)
+    out = torch.full_like(q, UNWRITTEN)
+    ca.full(q, k, v, out=out, scale=w.scale)
     torch.cuda.synchronize()
     check_any_size_properties(out, v)
     rows = sample_rows(1, w.L, w.H, np.random.default_rng(3), per=40)

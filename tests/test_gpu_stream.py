@@ -142,9 +142,17 @@ def test_stream_workload_sampled_parity():
     S, depth, tail = 9, 8, 4
     say("case stream workload", S, depth, w)
     q, k, v = synth.queue_inputs(S, w.L, w.H, w.D, 7, device=DEV, k_rho=0.9)
-    out = torch.empty_like(q)
+    out = torch.full_like(q, SENTINEL)
     ca.ring_step(q, k, v, out, tail, depth, scale=w.scale)
     torch.cuda.synchronize()
+    live = [(tail - c) % S for c in range(depth)]
+    vmax = v.float().abs().amax().item()
+    for s_ in range(S):
+        if s_ in live:
+            assert torch.isfinite(out[s_]).all()
+            assert out[s_].float().abs().amax().item() <= vmax * (1 + 2 ** -7)
+        else:
+            assert (out[s_] == SENTINEL).all()
     rng = np.random.default_rng(7)
     rows = []
     for c in (0, 1, 4, 5, depth - 1):

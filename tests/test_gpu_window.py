@@ -199,8 +199,10 @@ def test_window_workload_sampled_parity():
     q, k, v = synth.queue_inputs(w.n, w.L, w.H, w.D, w.seed, device=DEV, k_rho=w.k_rho,
                                  v_rho=w.v_rho)
     cache = synth.build_cache(k, v)
-    out = ca.window_step(q, k, v, cache, scale=w.scale)
+    out = torch.full((w.n, 2, w.L, w.H, w.D), SENTINEL, dtype=q.dtype, device=DEV)
+    ca.window_step(q, k, v, cache, out=out, scale=w.scale)
     torch.cuda.synchronize()
+    assert (out[w.n - 1, 1] == SENTINEL).all()
     vals = valid_rows(out)
     assert torch.isfinite(vals).all()
     assert vals.float().abs().amax().item() <= v.float().abs().amax().item() * (1 + 2 ** -7)

@@ -83,6 +83,31 @@ def test_validate_queue_rejects(kw, code):
     assert msg
 
 
+G = 1 << 34  # fake addresses far enough apart for rows of a quarter million heads
+
+
+@pytest.mark.parametrize("H,D,dtype,code", [
+    (262143, 128, ca.BF16, ca.OK),            # 64 rows span 2^32 - 16 KiB
+    (262144, 128, ca.BF16, ca.EUNSUPPORTED),  # 64 rows span 2^32 bytes
+    (131071, 128, ca.F32, ca.OK),
+    (131072, 128, ca.F32, ca.EUNSUPPORTED),
+    (524288, 64, ca.BF16, ca.EUNSUPPORTED),
+])
+def test_validate_rejects_rows_beyond_32bit_tile_offsets(H, D, dtype, code):
+    """The kernels address a 64-row key/value tile by 32-bit byte offsets from
+    its first row, so 64 rows of heads * head_dim elements must span under
+    2^32 bytes; every entry point that launches the attention kernels checks it."""
+    rc, msg = vq(q=G, k=2 * G, v=3 * G, out=4 * G, L=1, n=1, H=H, D=D, dtype=dtype)
+    assert rc == code, msg
+    rc, msg = vf(q=G, k=2 * G, v=3 * G, out=4 * G, B=1, lq=1, lkv=1, H=H, D=D, dtype=dtype)
+    assert rc == code, msg
+    rc, msg = vw(q=G, k=2 * G, v=3 * G, out=5 * G, L=1, n=1, H=H, D=D, dtype=dtype)
+    assert rc == code, msg
+    rc, msg = vr(q=G, k=2 * G, v=3 * G, out=4 * G, S=1, tail=0, n=1, L=1, H=H, D=D,
+                 dtype=dtype)
+    assert rc == code, msg
+
+
 def vf(**kw):
     a = dict(q=P, k=2 * P, v=3 * P, out=4 * P, B=2, lq=16, lkv=8, stride=0, H=2, D=128,
              scale=0.1, dtype=ca.BF16)

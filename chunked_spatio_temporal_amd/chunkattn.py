@@ -55,6 +55,9 @@ def load_library():
     lib.chunkattn_destroy.argtypes = [vp]
     lib.chunkattn_queue_step.restype = i32
     lib.chunkattn_queue_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
+    lib.chunkattn_queue_step_noalloc.restype = i32
+    lib.chunkattn_queue_step_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                                 i32, vp]
     lib.chunkattn_full.restype = i32
     lib.chunkattn_full.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, f32, i32, vp]
     lib.chunkattn_validate_queue_step.restype = i32
@@ -214,6 +217,24 @@ def queue_step(q, k, v, kv_cache=None, out=None, scale=None, stream=None, ctx=No
     scale = D ** -0.5 if scale is None else float(scale)
     ctx = ctx or create(q.device.index or 0)
     rc = load_library().chunkattn_queue_step(
+        ctx.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_cache), _ptr(out), L, n, H, D, scale,
+        _dtype_code(q), _stream(q, stream))
+    _check(rc, ctx.handle)
+    return out
+
+
+def queue_step_noalloc(q, k, v, kv_cache, out, scale=None, stream=None, ctx=None):
+    """The queue step through chunkattn_queue_step_noalloc: same result as
+    queue_step, with the work queue in the library's static device scratch
+    (no allocation by the call; calls on one device must not overlap).  The
+    caller passes `out`.  Returns `out`."""
+    n, L, H, D = _queue_args("queue_step_noalloc", q, k, v, kv_cache)
+    _require(out, "out", q.device)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("chunkattn.queue_step_noalloc: out must match q")
+    scale = D ** -0.5 if scale is None else float(scale)
+    ctx = ctx or create(q.device.index or 0)
+    rc = load_library().chunkattn_queue_step_noalloc(
         ctx.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_cache), _ptr(out), L, n, H, D, scale,
         _dtype_code(q), _stream(q, stream))
     _check(rc, ctx.handle)

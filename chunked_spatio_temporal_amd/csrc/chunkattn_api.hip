@@ -29,6 +29,17 @@ constexpr int kQueueSlots = 64;
 constexpr int kCaptureSlots = 448;
 constexpr int kQueueWords = 16;
 
+// Scratch of chunkattn_queue_step_noalloc: one work-queue slot (16 claim words,
+// 128 bytes) in a static device array, so that entry point needs no memory
+// from the context.  Each device the library runs on holds its own copy until
+// the process ends.  In host code `scratch` only stands in for the symbol and
+// is never passed to a kernel: chunkattn_create looks up the array's device
+// address with hipGetSymbolAddress (the device current) and the context keeps
+// it; kernels and the clearing kernel get that address.  Every noalloc call on
+// a device shares the array, so such calls must not overlap on one device.
+constexpr int kStaticScratchWords = 16;
+static __device__ __align__(256) unsigned long long scratch[kStaticScratchWords];
+
 struct chunkattn_ctx {
   int device = 0;
   int n_cu = 0;
@@ -36,6 +47,8 @@ struct chunkattn_ctx {
   int waves = 8;  // waves per workgroup; a work item covers 32 * waves query rows
   // device, (kQueueSlots + kCaptureSlots) * kQueueWords words
   unsigned long long* queue = nullptr;
+  // device address of this device's `scratch` array (noalloc entry point)
+  unsigned long long* static_scratch = nullptr;
   std::atomic<unsigned> next_slot{0};
   std::atomic<unsigned> next_capture{0};
   std::string arch;
@@ -295,13 +308,25 @@ struct DeviceGuard {
   }
 };
 
-int run(chunkattn_ctx* ctx, const KernelArgs& args, int head_dim, int dtype, void* stream) {
+// Launches the main pass (and the recheck) of a prepared argument block.
+// fixed_queue: NULL = the work-queue slot comes from the context's buffer;
+// otherwise the persistent pass uses these kStaticScratchWords words (the
+// noalloc entry point's static scratch).
+int run(chunkattn_ctx* ctx, const KernelArgs& args, int head_dim, int dtype, void* stream,
+        unsigned long long* fixed_queue = nullptr) {
   DeviceGuard g(ctx->device);
   if (!g.ok) return set_err(&ctx->err, CHUNKATTN_EDEVICE, "cannot make device %d current",
                             ctx->device);
   KernelArgs a = args;
   a.queue = nullptr;
-  if (ctx->waves == 8) {
+  if (ctx->waves == 8 && fixed_queue) {
+    // one claim word per die must fit in the static scratch
+    if (a.plan.n_xcd > kStaticScratchWords)
+      return set_err(&ctx->err, CHUNKATTN_EUNSUPPORTED,
+                     "device has %d dies; the static work queue holds %d claim words",
+                     a.plan.n_xcd, kStaticScratchWords);
+    a.queue = fixed_queue;
+  } else if (ctx->waves == 8) {
     // one claim word per die must fit in a slot
     if (a.plan.n_xcd > kQueueWords) a.plan.n_xcd = 1;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -394,6 +419,32 @@ int chunkattn_create(chunkattn_ctx** out, int device_ordinal, unsigned flags) {
     }
     ctx->queue = static_cast<unsigned long long*>(q);
   }
+  {
+    // the noalloc entry point's static scratch on this device, and the LDS
+    // limit of the 256-row kernels, set up once here so that hot calls do
+    // neither
+    DeviceGuard g(device_ordinal);
+    void* p = nullptr;
+    const hipError_t es = g.ok ? hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) : hipErrorInvalidDevice;
+    if (es != hipSuccess || !p) {
+      if (ctx->queue) (void)hipFree(ctx->queue);
+      delete ctx;
+      return set_err(&g_thread_err, CHUNKATTN_EDEVICE,
+                     "device %d: cannot locate the static scratch buffer (%s)", device_ordinal,
+                     hipGetErrorString(es));
+    }
+    ctx->static_scratch = static_cast<unsigned long long*>(p);
+    if (allow_pingpong_lds<128, __bf16>() != hipSuccess ||
+        allow_pingpong_lds<128, float>() != hipSuccess ||
+        allow_pingpong_lds<64, __bf16>() != hipSuccess ||
+        allow_pingpong_lds<64, float>() != hipSuccess) {
+      if (ctx->queue) (void)hipFree(ctx->queue);
+      delete ctx;
+      return set_err(&g_thread_err, CHUNKATTN_EDEVICE,
+                     "device %d: cannot raise the LDS limit of the 256-row kernels",
+                     device_ordinal);
+    }
+  }
   *out = ctx;
   return CHUNKATTN_OK;
 }
@@ -426,9 +477,16 @@ int chunkattn_validate_full(const void* q, const void* k, const void* v, const v
                        head_dim, scale, dtype);
 }
 
-int chunkattn_queue_step(chunkattn_ctx* ctx, const void* q, const void* k, const void* v,
-                         const void* kv_cache, void* out, int chunk_len, int n_chunks,
-                         int heads, int head_dim, float scale, int dtype, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Body of chunkattn_queue_step and chunkattn_queue_step_noalloc
+// (fixed_queue: see run()).
+int queue_step_impl(chunkattn_ctx* ctx, const void* q, const void* k, const void* v,
+                    const void* kv_cache, void* out, int chunk_len, int n_chunks, int heads,
+                    int head_dim, float scale, int dtype, void* hip_stream,
+                    unsigned long long* fixed_queue) {
   if (!ctx) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "ctx must be non-NULL");
   int rc = validate_queue(&ctx->err, q, k, v, kv_cache, out, chunk_len, n_chunks, heads,
                           head_dim, scale, dtype);
@@ -462,7 +520,30 @@ int chunkattn_queue_step(chunkattn_ctx* ctx, const void* q, const void* k, const
   }
   a.row_stride = heads * head_dim;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  return run(ctx, a, head_dim, dtype, hip_stream);
+  return run(ctx, a, head_dim, dtype, hip_stream, fixed_queue);
+}
+
+}  // namespace
+
+extern "C" {
+
+int chunkattn_queue_step(chunkattn_ctx* ctx, const void* q, const void* k, const void* v,
+                         const void* kv_cache, void* out, int chunk_len, int n_chunks,
+                         int heads, int head_dim, float scale, int dtype, void* hip_stream) {
+  return queue_step_impl(ctx, q, k, v, kv_cache, out, chunk_len, n_chunks, heads, head_dim,
+                         scale, dtype, hip_stream, nullptr);
+}
+
+int chunkattn_queue_step_noalloc(chunkattn_ctx* ctx, const void* q, const void* k,
+                                 const void* v, const void* kv_cache, void* out, int chunk_len,
+                                 int n_chunks, int heads, int head_dim, float scale, int dtype,
+                                 void* hip_stream) {
+  if (!ctx) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "ctx must be non-NULL");
+  if (!ctx->static_scratch)
+    return set_err(&ctx->err, CHUNKATTN_EDEVICE, "no static scratch buffer on device %d",
+                   ctx->device);
+  return queue_step_impl(ctx, q, k, v, kv_cache, out, chunk_len, n_chunks, heads, head_dim,
+                         scale, dtype, hip_stream, ctx->static_scratch);
 }
 
 int chunkattn_full(chunkattn_ctx* ctx, const void* q, const void* k, const void* v, void* out,

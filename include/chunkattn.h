@@ -132,6 +132,26 @@ int chunkattn_queue_step(chunkattn_ctx *ctx, const void *q, const void *k, const
                          int heads, int head_dim, float scale, int dtype, void *hip_stream);
 
 /*
+ * For callers that cannot allocate device memory on the hot path (code under
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same queue step as chunkattn_queue_step, same arguments, layouts, errors and
+ * bit-identical results, except that the persistent main pass keeps its work
+ * queue in a static device array of the library (16 words, 128 bytes per
+ * device, held until the process ends) instead of the context's buffer.  The
+ * call allocates nothing, host or device.  The array's device address is
+ * looked up once per context by chunkattn_create.  All calls of this entry
+ * point on one device share that array, which a small kernel on hip_stream
+ * clears before every main pass: such calls must not overlap on one device
+ * (on different streams without ordering, or graph replays running at once),
+ * or they race.  Fails with CHUNKATTN_EUNSUPPORTED if the device has more
+ * dies than the array has claim words (16).
+ */
+int chunkattn_queue_step_noalloc(chunkattn_ctx *ctx, const void *q, const void *k,
+                                 const void *v, const void *kv_cache, void *out,
+                                 int chunk_len, int n_chunks, int heads, int head_dim,
+                                 float scale, int dtype, void *hip_stream);
+
+/*
  * One window step, the form the feature cache is introduced for in the
  * DualParal write-up (section 三): processing the window [B_{i-1}, B_i] of
  * two neighbouring chunks reuses the cached self-attention K/V of B_{i+1},

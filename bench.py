@@ -38,6 +38,15 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def kernel_name(block_rows: int, D: int, dtype: str) -> str:
+    """The main-pass kernel a call with this work-item size runs."""
+    if block_rows == 384:
+        return "chunk_attn_fwd_wide"
+    if block_rows == 256:
+        return f"chunk_attn_fwd_pingpong<{D},{dtype}>"
+    return f"chunk_attn_fwd<{D},{dtype},{block_rows // 32}>"
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -49,7 +58,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--block-rows", type=int, default=0, choices=(0, 128, 256),
+    ap.add_argument("--block-rows", type=int, default=0, choices=(0, 128, 256, 384),
                     help="query rows per work item (0: library default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (counter calibration)")
@@ -112,7 +121,8 @@ def main():
           flush=True)
 
     stream = torch.cuda.current_stream(dev)
-    flags = {0: 0, 128: ca.FLAG_BLOCK128, 256: ca.FLAG_BLOCK256}[args.block_rows]
+    flags = {0: 0, 128: ca.FLAG_BLOCK128, 256: ca.FLAG_BLOCK256,
+             384: ca.FLAG_BLOCK384}[args.block_rows]
     ctx = ca.create(0, flags)
 
     if w.kind == "stream":
@@ -179,8 +189,8 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
         "traffic": None,
-        "kernel": (f"chunk_attn_fwd_pingpong<{w.D},{w.dtype}>" if ctx.block_rows == 256
-                   else f"chunk_attn_fwd<{w.D},{w.dtype},{ctx.block_rows // 32}>"),
+        "kernel": kernel_name(ctx.call_block_rows(w.D, ca.BF16 if w.dtype == "bf16" else ca.F32),
+                              w.D, w.dtype),
         "launch_ms_avg": round(dom_avg_ms, 4),
         "launch_ms_min": round(float(launch_ms.min()), 4),
         "launch_ms_p90": round(float(np.percentile(launch_ms, 90)), 4),

@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "chunkattn.h")
 
 OK, EINVAL, EUNSUPPORTED, EDEVICE, ENOMEM, ELAUNCH = range(6)
 BF16, F32 = 0, 1
-FLAG_BLOCK128, FLAG_BLOCK256 = 1, 2
+FLAG_BLOCK128, FLAG_BLOCK256, FLAG_BLOCK384 = 1, 2, 4
 PLAN_FIELDS = ("chunk", "head", "q_row0", "q_rows", "pred_chunk", "pred_rows", "own_rows")
 
 
@@ -49,6 +49,8 @@ def load_library():
     lib.chunkattn_block_rows.restype = i32
     lib.chunkattn_ctx_block_rows.restype = i32
     lib.chunkattn_ctx_block_rows.argtypes = [vp]
+    lib.chunkattn_ctx_call_block_rows.restype = i32
+    lib.chunkattn_ctx_call_block_rows.argtypes = [vp, i32, i32]
     lib.chunkattn_create.restype = i32
     lib.chunkattn_create.argtypes = [ctypes.POINTER(vp), i32, ctypes.c_uint]
     lib.chunkattn_destroy.restype = i32
@@ -155,7 +157,13 @@ class Context:
 
     @property
     def block_rows(self) -> int:
+        """Query rows per work item of a bf16, head_dim-128 call."""
         return int(load_library().chunkattn_ctx_block_rows(self.handle))
+
+    def call_block_rows(self, head_dim: int, dtype: int) -> int:
+        """Query rows per work item of a call with this head_dim and dtype code."""
+        return int(load_library().chunkattn_ctx_call_block_rows(self.handle, int(head_dim),
+                                                                int(dtype)))
 
 
 _contexts: dict[tuple, Context] = {}

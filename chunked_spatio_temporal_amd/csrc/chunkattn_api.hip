@@ -13,6 +13,7 @@
 
 #include "attn_kernel.h"
 #include "attn_pingpong.h"
+#include "attn_wide.h"
 #include "chunkattn.h"
 #include "fifo.h"
 #include "noise.h"
@@ -44,7 +45,9 @@ struct chunkattn_ctx {
   int device = 0;
   int n_cu = 0;
   int n_xcd = 1;
-  int waves = 8;  // waves per workgroup; a work item covers 32 * waves query rows
+  // query rows per work item: 128, 256 or 384 (fixed by the flags), or 0 for
+  // the default (call_block_rows)
+  int block_rows = 0;
   // device, (kQueueSlots + kCaptureSlots) * kQueueWords words
   unsigned long long* queue = nullptr;
   // device address of this device's `scratch` array (noalloc entry point)
@@ -60,8 +63,19 @@ namespace {
 using chunkattn::KernelArgs;
 using chunkattn::Plan;
 
-constexpr int kDefaultWaves = 8;
-constexpr int kMinBlockRows = 128;  // smallest work item (4 waves); bounds the grid
+constexpr int kDefaultBlockRows = 256;  // default work item for every call but bf16/128
+constexpr int kMinBlockRows = 128;      // smallest work item (4 waves); bounds the grid
+
+// Query rows per work item of one call: the context's fixed size, or by
+// default 256 (ping-pong kernel).
+int call_block_rows(const chunkattn_ctx* ctx, int head_dim, int dtype) {
+  (void)head_dim;
+  (void)dtype;
+  return ctx->block_rows ? ctx->block_rows : kDefaultBlockRows;
+}
+
+// The 384-row kernel exists for bf16 storage and head_dim 128 only.
+bool wide_supported(int head_dim, int dtype) { return head_dim == 128 && dtype == CHUNKATTN_BF16; }
 
 thread_local std::string g_thread_err;
 
@@ -288,10 +302,42 @@ hipError_t launch_w(const KernelArgs& a, int n_persist, int head_dim, int dtype,
                                  : launch_t<64, float, W>(a, n_persist, stream);
 }
 
-hipError_t launch(const KernelArgs& a, int waves, int n_persist, int head_dim, int dtype,
+// The 384-row main pass (48 rows per wave, persistent like the 256-row one),
+// then its recheck (three 128-row items per marked item).
+hipError_t launch_wide(const KernelArgs& a, int n_persist, hipStream_t stream) {
+  if (!a.queue || n_persist < 1 || a.plan.n_xcd > kQueueWords) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(chunkattn::queue_clear, dim3(1), dim3(64), 0, stream, a.queue,
+                     a.plan.n_xcd);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(chunkattn::chunk_attn_fwd_wide, dim3((unsigned)n_persist), dim3(512),
+                     chunkattn::kPingPongLdsBytes<128>, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(chunkattn::chunk_attn_recheck_wide<4>, dim3((unsigned)a.plan.n_items),
+                     dim3(256), chunkattn::kSyncLdsBytes<128>, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch(const KernelArgs& a, int block_rows, int n_persist, int head_dim, int dtype,
                   hipStream_t stream) {
-  return waves == 4 ? launch_w<4>(a, n_persist, head_dim, dtype, stream)
-                    : launch_w<8>(a, n_persist, head_dim, dtype, stream);
+  if (block_rows == 384) return launch_wide(a, n_persist, stream);
+  return block_rows == 128 ? launch_w<4>(a, n_persist, head_dim, dtype, stream)
+                           : launch_w<8>(a, n_persist, head_dim, dtype, stream);
+}
+
+hipError_t allow_wide_lds() {
+  static std::atomic<uint64_t> done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunkattn::chunk_attn_fwd_wide),
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)chunkattn::kPingPongLdsBytes<128>);
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
 }
 
 // Makes the context's device current for the duration of a call.
@@ -319,14 +365,18 @@ int run(chunkattn_ctx* ctx, const KernelArgs& args, int head_dim, int dtype, voi
                             ctx->device);
   KernelArgs a = args;
   a.queue = nullptr;
-  if (ctx->waves == 8 && fixed_queue) {
+  const int bm = a.plan.bm;
+  if (bm == 384 && !wide_supported(head_dim, dtype))
+    return set_err(&ctx->err, CHUNKATTN_EUNSUPPORTED,
+                   "384-row work items need bf16 storage and head_dim 128");
+  if (bm >= 256 && fixed_queue) {
     // one claim word per die must fit in the static scratch
     if (a.plan.n_xcd > kStaticScratchWords)
       return set_err(&ctx->err, CHUNKATTN_EUNSUPPORTED,
                      "device has %d dies; the static work queue holds %d claim words",
                      a.plan.n_xcd, kStaticScratchWords);
     a.queue = fixed_queue;
-  } else if (ctx->waves == 8) {
+  } else if (bm >= 256) {
     // one claim word per die must fit in a slot
     if (a.plan.n_xcd > kQueueWords) a.plan.n_xcd = 1;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -348,7 +398,7 @@ int run(chunkattn_ctx* ctx, const KernelArgs& args, int head_dim, int dtype, voi
   }
   const int n_persist = (int)(a.plan.n_items < ctx->n_cu ? a.plan.n_items : ctx->n_cu);
   const hipError_t e =
-      launch(a, ctx->waves, n_persist, head_dim, dtype, static_cast<hipStream_t>(stream));
+      launch(a, bm, n_persist, head_dim, dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return set_err(&ctx->err, CHUNKATTN_ELAUNCH, "kernel launch failed: %s",
                    hipGetErrorString(e));
@@ -367,15 +417,21 @@ Plan window_plan(int L, int n, int heads, int bm, int n_xcd) {
 
 extern "C" {
 
-int chunkattn_block_rows(void) { return 32 * kDefaultWaves; }
+int chunkattn_block_rows(void) { return kDefaultBlockRows; }
 
-int chunkattn_ctx_block_rows(const chunkattn_ctx* ctx) { return ctx ? 32 * ctx->waves : 0; }
+int chunkattn_ctx_block_rows(const chunkattn_ctx* ctx) {
+  return ctx ? call_block_rows(ctx, 128, CHUNKATTN_BF16) : 0;
+}
+
+int chunkattn_ctx_call_block_rows(const chunkattn_ctx* ctx, int head_dim, int dtype) {
+  return ctx ? call_block_rows(ctx, head_dim, dtype) : 0;
+}
 
 int chunkattn_create(chunkattn_ctx** out, int device_ordinal, unsigned flags) {
   if (!out) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "out must be non-NULL");
   *out = nullptr;
-  const unsigned known = CHUNKATTN_FLAG_BLOCK128 | CHUNKATTN_FLAG_BLOCK256;
-  if ((flags & ~known) != 0 || flags == known)
+  const unsigned known = CHUNKATTN_FLAG_BLOCK128 | CHUNKATTN_FLAG_BLOCK256 | CHUNKATTN_FLAG_BLOCK384;
+  if ((flags & ~known) != 0 || (flags & (flags - 1)) != 0)
     return set_err(&g_thread_err, CHUNKATTN_EINVAL, "unknown or conflicting flags 0x%x", flags);
   int count = 0;
   if (hipGetDeviceCount(&count) != hipSuccess || device_ordinal < 0 || device_ordinal >= count)
@@ -391,8 +447,10 @@ int chunkattn_create(chunkattn_ctx** out, int device_ordinal, unsigned flags) {
   chunkattn_ctx* ctx = new (std::nothrow) chunkattn_ctx();
   if (!ctx) return set_err(&g_thread_err, CHUNKATTN_ENOMEM, "context allocation failed");
   ctx->device = device_ordinal;
-  ctx->waves = (flags & CHUNKATTN_FLAG_BLOCK128) ? 4 : (flags & CHUNKATTN_FLAG_BLOCK256) ? 8
-                                                                                       : kDefaultWaves;
+  ctx->block_rows = flags == CHUNKATTN_FLAG_BLOCK128   ? 128
+                    : flags == CHUNKATTN_FLAG_BLOCK256 ? 256
+                    : flags == CHUNKATTN_FLAG_BLOCK384 ? 384
+                                                       : 0;
   ctx->n_cu = prop.multiProcessorCount;
   ctx->arch = prop.gcnArchName;
   int xcc = 0;
@@ -400,7 +458,7 @@ int chunkattn_create(chunkattn_ctx** out, int device_ordinal, unsigned flags) {
           hipSuccess &&
       xcc > 0)
     ctx->n_xcd = xcc;
-  if (ctx->waves == 8) {
+  if (ctx->block_rows != 128) {
     // the work queues of the persistent main pass (each launch clears its own)
     DeviceGuard g(device_ordinal);
     const size_t bytes =
@@ -434,7 +492,7 @@ int chunkattn_create(chunkattn_ctx** out, int device_ordinal, unsigned flags) {
                      hipGetErrorString(es));
     }
     ctx->static_scratch = static_cast<unsigned long long*>(p);
-    if (allow_pingpong_lds<128, __bf16>() != hipSuccess ||
+    if (allow_wide_lds() != hipSuccess || allow_pingpong_lds<128, __bf16>() != hipSuccess ||
         allow_pingpong_lds<128, float>() != hipSuccess ||
         allow_pingpong_lds<64, __bf16>() != hipSuccess ||
         allow_pingpong_lds<64, float>() != hipSuccess) {
@@ -499,7 +557,7 @@ int queue_step_impl(chunkattn_ctx* ctx, const void* q, const void* k, const void
   const size_t es = elem_size(dtype);
   KernelArgs a{};  // zero: linear batch entries unless set below
   a.plan = chunkattn::make_plan(n_chunks, 1, heads, chunk_len, chunk_len, chunk_len,
-                                32 * ctx->waves, ctx->n_xcd);
+                                call_block_rows(ctx, head_dim, dtype), ctx->n_xcd);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -558,7 +616,8 @@ int chunkattn_full(chunkattn_ctx* ctx, const void* q, const void* k, const void*
     return CHUNKATTN_OK;
   }
   KernelArgs a{};  // zero: linear batch entries unless set below
-  a.plan = chunkattn::make_plan(batch, batch, heads, lq, lkv, 0, 32 * ctx->waves, ctx->n_xcd);
+  a.plan = chunkattn::make_plan(batch, batch, heads, lq, lkv, 0,
+                                call_block_rows(ctx, head_dim, dtype), ctx->n_xcd);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -598,7 +657,8 @@ int chunkattn_window_step(chunkattn_ctx* ctx, const void* q, const void* k, cons
   const int64_t per_chunk = (int64_t)chunk_len * heads * head_dim;
   const size_t es = elem_size(dtype);
   KernelArgs a{};  // zero: linear batch entries unless set below
-  a.plan = window_plan(chunk_len, n_chunks, heads, 32 * ctx->waves, ctx->n_xcd);
+  a.plan = window_plan(chunk_len, n_chunks, heads, call_block_rows(ctx, head_dim, dtype),
+                       ctx->n_xcd);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -626,9 +686,9 @@ int chunkattn_window_plan_debug(int chunk_len, int n_chunks, int heads, int n_xc
                                 int block_rows, int* items, long long cap, long long* n_items) {
   g_thread_err.clear();
   if (!n_items) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "n_items must be non-NULL");
-  if (block_rows == 0) block_rows = 32 * kDefaultWaves;
+  if (block_rows == 0) block_rows = kDefaultBlockRows;
   if (chunk_len < 0 || n_chunks < 0 || heads < 1 || cap < 0 || (cap > 0 && !items) ||
-      (block_rows != 128 && block_rows != 256))
+      (block_rows != 128 && block_rows != 256 && block_rows != 384))
     return set_err(&g_thread_err, CHUNKATTN_EINVAL, "bad window_plan_debug arguments");
   *n_items = 0;
   if (chunk_len == 0 || n_chunks == 0) return CHUNKATTN_OK;
@@ -673,7 +733,7 @@ int chunkattn_ring_step(chunkattn_ctx* ctx, const void* q_ring, const void* k_ri
   const int64_t per_chunk = (int64_t)chunk_len * heads * head_dim;
   KernelArgs a{};
   a.plan = chunkattn::make_plan(n_live, 1, heads, chunk_len, chunk_len, chunk_len,
-                                32 * ctx->waves, ctx->n_xcd);
+                                call_block_rows(ctx, head_dim, dtype), ctx->n_xcd);
   a.q = q_ring;
   a.k = k_ring;
   a.v = v_ring;
@@ -866,9 +926,9 @@ int chunkattn_plan_debug(int chunk_len, int n_chunks, int heads, int n_xcd, int 
                          int* items, long long cap, long long* n_items) {
   g_thread_err.clear();
   if (!n_items) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "n_items must be non-NULL");
-  if (block_rows == 0) block_rows = 32 * kDefaultWaves;
+  if (block_rows == 0) block_rows = kDefaultBlockRows;
   if (chunk_len < 0 || n_chunks < 0 || heads < 1 || cap < 0 || (cap > 0 && !items) ||
-      (block_rows != 128 && block_rows != 256))
+      (block_rows != 128 && block_rows != 256 && block_rows != 384))
     return set_err(&g_thread_err, CHUNKATTN_EINVAL, "bad plan_debug arguments");
   *n_items = 0;
   if (chunk_len == 0 || n_chunks == 0) return CHUNKATTN_OK;
@@ -897,7 +957,7 @@ int chunkattn_plan_device(chunkattn_ctx* ctx, int chunk_len, int n_chunks, int h
     return set_err(&ctx->err, CHUNKATTN_EINVAL, "bad plan_device arguments");
   if (chunk_len == 0 || n_chunks == 0 || cap == 0) return CHUNKATTN_OK;
   const Plan p = chunkattn::make_plan(n_chunks, 1, heads, chunk_len, chunk_len, chunk_len,
-                                      32 * ctx->waves, ctx->n_xcd);
+                                      call_block_rows(ctx, 128, CHUNKATTN_BF16), ctx->n_xcd);
   const int64_t n = p.n_items < cap ? p.n_items : cap;
   DeviceGuard g(ctx->device);
   if (!g.ok) return set_err(&ctx->err, CHUNKATTN_EDEVICE, "cannot make device current");

@@ -92,6 +92,9 @@ typedef enum {
 /* chunkattn_create flags: query rows per work item (one workgroup). */
 #define CHUNKATTN_FLAG_BLOCK128 1u /* 128 rows, 4 waves, two workgroups per CU */
 #define CHUNKATTN_FLAG_BLOCK256 2u /* 256 rows, 8 waves, one workgroup per CU */
+#define CHUNKATTN_FLAG_BLOCK384 4u /* 384 rows, 8 waves of 48 rows, one workgroup per CU;
+                                      bf16 and head_dim 128 only (other calls fail with
+                                      CHUNKATTN_EUNSUPPORTED) */
 
 /* Query rows per work item of a context created with flags = 0. */
 int chunkattn_block_rows(void);
@@ -107,8 +110,13 @@ int chunkattn_block_rows(void);
  */
 int chunkattn_create(chunkattn_ctx **out, int device_ordinal, unsigned flags);
 
-/* Query rows per work item of this context (128 or 256). */
+/* Query rows per work item of this context for a bf16, head_dim-128 call
+ * (128, 256 or 384). */
 int chunkattn_ctx_block_rows(const chunkattn_ctx *ctx);
+
+/* Query rows per work item of this context for a call with the given
+ * head_dim and dtype. */
+int chunkattn_ctx_call_block_rows(const chunkattn_ctx *ctx, int head_dim, int dtype);
 
 /* Releases a context (NULL is accepted). */
 int chunkattn_destroy(chunkattn_ctx *ctx);

@@ -52,9 +52,13 @@ __device__ __forceinline__ int wide_vswz(int r) { return 2 * (r & 7); }   // 16-
 __device__ __forceinline__ void pin(f32x4_t& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(u32x4_t& x) { asm volatile("" : "+v"(x)); }
 
-// One 384-row work item (head_dim 128, bf16).  after_prologue() runs once in
-// every thread, after the prologue's barrier.
-template <typename AfterPrologue>
+// One work item of up to 384 rows (head_dim 128, bf16), with kQB 16-row query
+// blocks per wave: wave w takes rows [16*kQB*w, 16*kQB*(w+1)) of the item.
+// kQB = 3 covers 384 rows; an item with at most 256 (128) rows, the last
+// query tile of a chunk, runs with kQB = 2 (1): its matrix phases shrink to
+// 64 (32) MFMAs instead of padding the missing rows.  after_prologue() runs
+// once in every thread, after the prologue's barrier.
+template <int kQB, typename AfterPrologue>
 __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& it,
                                                unsigned char* smem,
                                                AfterPrologue&& after_prologue) {
@@ -64,7 +68,8 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
   constexpr int W = kWideWaves;
   constexpr int kCpw = G::kChunks / W;  // 1 KB load chunks per wave per tile (2)
   static_assert(kCpw == 2, "two 1 KB chunks per wave");
-  constexpr int kQB = kWideRows / 16;   // query blocks per wave (3)
+  static_assert(kQB >= 1 && kQB * 16 <= kWideRows, "query blocks per wave");
+  constexpr int kRowsW = 16 * kQB;      // query rows per wave
   constexpr int kKS = D / 32;           // 32-dim steps of S (4)
   constexpr int kKB = kBN / 16;         // 16-key blocks of S (4)
   constexpr int kDB = D / 16;           // 16-dim blocks of O (8)
@@ -121,7 +126,7 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
   u32x4_t qf[kQB][kKS];
 #pragma unroll
   for (int q3 = 0; q3 < kQB; ++q3) {
-    const int r = wave * kWideRows + q3 * 16 + j;
+    const int r = wave * kRowsW + q3 * 16 + j;
     const bool valid = r < it.q_rows;
     const T* qrow = qb + (int64_t)(it.q0 + r) * rs + g * 8;
 #pragma unroll
@@ -397,7 +402,7 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
   }
 #pragma unroll
   for (int q3 = 0; q3 < kQB; ++q3) {
-    const int r = wave * kWideRows + q3 * 16 + j;
+    const int r = wave * kRowsW + q3 * 16 + j;
     if (r < it.q_rows) {
       const float inv = 1.0f / l_tot[q3];
       T* orow = ob + (int64_t)(it.q0 + r) * rs + 4 * g;
@@ -445,7 +450,7 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_fwd_wide(KernelArgs a) {
       k = used_up;
       if (k < nx) ticket = atomicAdd(&a.queue[die_at(k)], 1ull);
     }
-    attn_item_wide(a, decode(a.plan, w), smem, [&]() __attribute__((always_inline)) {
+    auto after_prologue = [&]() __attribute__((always_inline)) {
       if (threadIdx.x == 0) {
         long long nw = -1;
         if (k < nx) {
@@ -454,7 +459,14 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_fwd_wide(KernelArgs a) {
         }
         next_item = nw;
       }
-    });
+    };
+    const Item it = decode(a.plan, w);
+    if (it.q_rows > 2 * 16 * kWideWaves)
+      attn_item_wide<3>(a, it, smem, after_prologue);
+    else if (it.q_rows > 16 * kWideWaves)
+      attn_item_wide<2>(a, it, smem, after_prologue);
+    else
+      attn_item_wide<1>(a, it, smem, after_prologue);
     wg_barrier();
     w = next_item;
     if (w == -2) {

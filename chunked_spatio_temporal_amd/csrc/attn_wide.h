@@ -57,10 +57,11 @@ __device__ __forceinline__ void pin(u32x4_t& x) { asm volatile("" : "+v"(x)); }
 // kQB = 3 covers 384 rows; an item with at most 256 (128) rows, the last
 // query tile of a chunk, runs with kQB = 2 (1): its matrix phases shrink to
 // 64 (32) MFMAs instead of padding the missing rows.  after_prologue() runs
-// once in every thread, after the prologue's barrier.
+// once in every thread, after the prologue's barrier.  A wave whose rows left
+// fp32's range sets *range_flag (LDS); the caller marks the item.
 template <int kQB, typename AfterPrologue>
 __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& it,
-                                               unsigned char* smem,
+                                               unsigned char* smem, int* range_flag,
                                                AfterPrologue&& after_prologue) {
   using T = __bf16;
   constexpr int D = 128;
@@ -122,28 +123,33 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
   const uint64_t kown_s = (uint64_t)(uintptr_t)kown - pshift, vown_s = (uint64_t)(uintptr_t)vown - pshift;
 
   // ---- Q^T fragments: B operand of S^T = K.Q^T; lane (j, g) holds dims
-  // 32*ks + 8g .. +7 of query row 16*qb + j of this wave's 48
+  // 32*ks + 8g .. +7 of query row 16*qb + j of this wave's rows (loaded in
+  // the prologue, after the first key/value loads are on their way)
   u32x4_t qf[kQB][kKS];
+  auto load_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int q3 = 0; q3 < kQB; ++q3) {
-    const int r = wave * kRowsW + q3 * 16 + j;
-    const bool valid = r < it.q_rows;
-    const T* qrow = qb + (int64_t)(it.q0 + r) * rs + g * 8;
+    for (int q3 = 0; q3 < kQB; ++q3) {
+      const int r = wave * kRowsW + q3 * 16 + j;
+      const bool valid = r < it.q_rows;
+      const T* qrow = qb + (int64_t)(it.q0 + r) * rs + g * 8;
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks)
-      qf[q3][ks] = valid ? Io<T>::load8(qrow + ks * 32) : u32x4_t{0u, 0u, 0u, 0u};
-  }
+      for (int ks = 0; ks < kKS; ++ks)
+        qf[q3][ks] = valid ? Io<T>::load8(qrow + ks * 32) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
   // scaled by scale * log2 e (nearest-even): S^T comes out in the log2 domain
+  auto scale_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int q3 = 0; q3 < kQB; ++q3)
+    for (int q3 = 0; q3 < kQB; ++q3)
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks)
+      for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x = qf[q3][ks][w];
-        qf[q3][ks][w] = pack_bf16(__uint_as_float(x << 16) * a.scale_log2,
-                                  __uint_as_float(x & 0xffff0000u) * a.scale_log2);
-      }
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t x = qf[q3][ks][w];
+          qf[q3][ks][w] = pack_bf16(__uint_as_float(x << 16) * a.scale_log2,
+                                    __uint_as_float(x & 0xffff0000u) * a.scale_log2);
+        }
+  };
 
   // ---- per-lane DMA map: LDS chunk c = wave*2 + i of a tile receives tile
   // row 4c + g at physical block j (logical block j ^ swizzle(row))
@@ -358,13 +364,16 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
     end_softmax();
   };
 
-  // ---- prologue: K(0) lands, groups 1 and 2 start
+  // ---- prologue: the first three groups of key/value loads and the Q
+  // loads go out together (one memory latency for all), then Q is scaled
   load_one(0, smem + kslot(0), std::false_type{});
-  wait_vmem();
-  wg_barrier();
-  after_prologue();
   issue(1);
   issue(2);
+  load_q();
+  wait_vmem();
+  scale_q();
+  wg_barrier();
+  after_prologue();
   if (group_b) wg_barrier();  // group B runs one phase behind group A
 
   if (n_tiles == 1) {
@@ -392,14 +401,13 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
     for (int db = 0; db < kDB; ++db)
       acc += (oacc[q3][db][0] + oacc[q3][db][1]) + (oacc[q3][db][2] + oacc[q3][db][3]);
   }
-  bool low = false;
+  bool bad = !__builtin_isfinite(acc);
 #pragma unroll
-  for (int q3 = 0; q3 < kQB; ++q3) low = low || !(l_tot[q3] >= 0x1p-64f);
+  for (int q3 = 0; q3 < kQB; ++q3) bad = bad || !(l_tot[q3] >= 0x1p-64f);
+  // the range check folds into the workgroup's flag; after the barrier that
+  // ends the item, thread 0 marks the item for the recheck pass if it is set
+  if (__ballot(bad) != 0 && lane == 0) *range_flag = 1;
   T* ob = static_cast<T*>(a.o) + e * a.o_bstride + (int64_t)it.h * D;
-  if (__syncthreads_or(!__builtin_isfinite(acc) || low)) {
-    if (tid == 0) ob[(int64_t)it.q0 * rs] = overflow_marker<T>();
-    return;
-  }
 #pragma unroll
   for (int q3 = 0; q3 < kQB; ++q3) {
     const int r = wave * kRowsW + q3 * 16 + j;
@@ -421,6 +429,7 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_fwd_wide(KernelArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __shared__ long long next_item;  // >= 0 item, -1 none left, -2 claim again
   __shared__ int used_up;          // thread 0: dies (from our own on) found empty
+  __shared__ int range_flag;       // some row of the current item left fp32's range
   const int nx = a.plan.n_xcd;
   const int die = (int)(__builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) % (unsigned)nx);
   auto die_at = [&](int k) __attribute__((always_inline)) {
@@ -439,6 +448,7 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_fwd_wide(KernelArgs a) {
   };
   if (threadIdx.x == 0) {
     used_up = 0;
+    range_flag = 0;
     claim_sync();
   }
   __syncthreads();
@@ -462,12 +472,18 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_fwd_wide(KernelArgs a) {
     };
     const Item it = decode(a.plan, w);
     if (it.q_rows > 2 * 16 * kWideWaves)
-      attn_item_wide<3>(a, it, smem, after_prologue);
+      attn_item_wide<3>(a, it, smem, &range_flag, after_prologue);
     else if (it.q_rows > 16 * kWideWaves)
-      attn_item_wide<2>(a, it, smem, after_prologue);
+      attn_item_wide<2>(a, it, smem, &range_flag, after_prologue);
     else
-      attn_item_wide<1>(a, it, smem, after_prologue);
+      attn_item_wide<1>(a, it, smem, &range_flag, after_prologue);
     wg_barrier();
+    if (threadIdx.x == 0 && range_flag != 0) {
+      // the marker follows thread 0's own store of that element
+      static_cast<__bf16*>(a.o)[a.entry(it.b) * a.o_bstride + (int64_t)it.q0 * a.row_stride +
+                                (int64_t)it.h * 128] = overflow_marker<__bf16>();
+      range_flag = 0;
+    }
     w = next_item;
     if (w == -2) {
       wg_barrier();  // every wave has read next_item before thread 0 rewrites it

@@ -27,7 +27,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # device code of the attention kernels (the work plan and the kernel bodies);
 # the host code around them does not change what the counters measure
 KERNEL_SOURCES = [os.path.join(ROOT, "chunked_spatio_temporal_amd", "csrc", f)
-                  for f in ("attn_kernel.h", "attn_pingpong.h", "plan.h")]
+                  for f in ("attn_kernel.h", "attn_pingpong.h", "attn_wide.h", "plan.h")]
 
 
 def kernel_hash() -> str:

@@ -63,19 +63,19 @@ namespace {
 using chunkattn::KernelArgs;
 using chunkattn::Plan;
 
-constexpr int kDefaultBlockRows = 256;  // default work item for every call but bf16/128
-constexpr int kMinBlockRows = 128;      // smallest work item (4 waves); bounds the grid
-
-// Query rows per work item of one call: the context's fixed size, or by
-// default 256 (ping-pong kernel).
-int call_block_rows(const chunkattn_ctx* ctx, int head_dim, int dtype) {
-  (void)head_dim;
-  (void)dtype;
-  return ctx->block_rows ? ctx->block_rows : kDefaultBlockRows;
-}
+constexpr int kMinBlockRows = 128;  // smallest work item (4 waves); bounds the grid
 
 // The 384-row kernel exists for bf16 storage and head_dim 128 only.
 bool wide_supported(int head_dim, int dtype) { return head_dim == 128 && dtype == CHUNKATTN_BF16; }
+
+// Query rows per work item of one call.  Contexts of 128 or 256 rows use that
+// size for every call; the default context (and a 384-row one) uses 384-row
+// items where the 384-row kernel exists (bf16, head_dim 128) and 256-row items
+// for every other call.
+int call_block_rows(const chunkattn_ctx* ctx, int head_dim, int dtype) {
+  if (ctx->block_rows == 128 || ctx->block_rows == 256) return ctx->block_rows;
+  return wide_supported(head_dim, dtype) ? 384 : 256;
+}
 
 thread_local std::string g_thread_err;
 
@@ -367,8 +367,8 @@ int run(chunkattn_ctx* ctx, const KernelArgs& args, int head_dim, int dtype, voi
   a.queue = nullptr;
   const int bm = a.plan.bm;
   if (bm == 384 && !wide_supported(head_dim, dtype))
-    return set_err(&ctx->err, CHUNKATTN_EUNSUPPORTED,
-                   "384-row work items need bf16 storage and head_dim 128");
+    return set_err(&ctx->err, CHUNKATTN_ELAUNCH,
+                   "internal: 384-row work items planned for a call without that kernel");
   if (bm >= 256 && fixed_queue) {
     // one claim word per die must fit in the static scratch
     if (a.plan.n_xcd > kStaticScratchWords)
@@ -417,7 +417,7 @@ Plan window_plan(int L, int n, int heads, int bm, int n_xcd) {
 
 extern "C" {
 
-int chunkattn_block_rows(void) { return kDefaultBlockRows; }
+int chunkattn_block_rows(void) { return 384; }
 
 int chunkattn_ctx_block_rows(const chunkattn_ctx* ctx) {
   return ctx ? call_block_rows(ctx, 128, CHUNKATTN_BF16) : 0;
@@ -686,7 +686,7 @@ int chunkattn_window_plan_debug(int chunk_len, int n_chunks, int heads, int n_xc
                                 int block_rows, int* items, long long cap, long long* n_items) {
   g_thread_err.clear();
   if (!n_items) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "n_items must be non-NULL");
-  if (block_rows == 0) block_rows = kDefaultBlockRows;
+  if (block_rows == 0) block_rows = 384;
   if (chunk_len < 0 || n_chunks < 0 || heads < 1 || cap < 0 || (cap > 0 && !items) ||
       (block_rows != 128 && block_rows != 256 && block_rows != 384))
     return set_err(&g_thread_err, CHUNKATTN_EINVAL, "bad window_plan_debug arguments");
@@ -926,7 +926,7 @@ int chunkattn_plan_debug(int chunk_len, int n_chunks, int heads, int n_xcd, int 
                          int* items, long long cap, long long* n_items) {
   g_thread_err.clear();
   if (!n_items) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "n_items must be non-NULL");
-  if (block_rows == 0) block_rows = kDefaultBlockRows;
+  if (block_rows == 0) block_rows = 384;
   if (chunk_len < 0 || n_chunks < 0 || heads < 1 || cap < 0 || (cap > 0 && !items) ||
       (block_rows != 128 && block_rows != 256 && block_rows != 384))
     return set_err(&g_thread_err, CHUNKATTN_EINVAL, "bad plan_debug arguments");

@@ -33,7 +33,7 @@
  * Numerics.  Q.K^T and P.V run on bf16 matrix cores with fp32 accumulation and
  * an fp32 softmax; P is rounded to bf16 before the P.V product and the
  * softmax denominator is summed from the same rounded P, so a constant V comes
- * back bit-exactly.  With 256-row work items Q is multiplied by scale * log2 e
+ * back bit-exactly.  With 256- and 384-row work items Q is multiplied by scale * log2 e
  * and rounded to bf16 once per item (relative 2^-9 per element).  dtype F32 means fp32
  * storage in and out, rounded to bf16 (nearest-even) on load.  bf16 outputs are
  * rounded nearest-even.  Results are bitwise deterministic run to run, and the
@@ -89,14 +89,17 @@ typedef enum {
     CHUNKATTN_F32 = 1   /* fp32 storage in and out (operands rounded to bf16) */
 } chunkattn_dtype;
 
-/* chunkattn_create flags: query rows per work item (one workgroup). */
+/* chunkattn_create flags: query rows per work item (one workgroup).  With no
+ * flag (0) a context uses 384-row items for bf16, head_dim-128 calls and
+ * 256-row items for every other call; CHUNKATTN_FLAG_BLOCK384 asks for the
+ * same explicitly. */
 #define CHUNKATTN_FLAG_BLOCK128 1u /* 128 rows, 4 waves, two workgroups per CU */
-#define CHUNKATTN_FLAG_BLOCK256 2u /* 256 rows, 8 waves, one workgroup per CU */
-#define CHUNKATTN_FLAG_BLOCK384 4u /* 384 rows, 8 waves of 48 rows, one workgroup per CU;
-                                      bf16 and head_dim 128 only (other calls fail with
-                                      CHUNKATTN_EUNSUPPORTED) */
+#define CHUNKATTN_FLAG_BLOCK256 2u /* 256 rows, 8 waves of 32 rows, one workgroup per CU */
+#define CHUNKATTN_FLAG_BLOCK384 4u /* 384 rows, 8 waves of 48 rows, one workgroup per CU,
+                                      for bf16 head_dim 128 (256 rows otherwise) */
 
-/* Query rows per work item of a context created with flags = 0. */
+/* Query rows per work item of a bf16, head_dim-128 call on a context created
+ * with flags = 0 (384). */
 int chunkattn_block_rows(void);
 
 /*
@@ -329,7 +332,7 @@ const char *chunkattn_last_error(const chunkattn_ctx *ctx);
  * pred_chunk is c-1 when the chunk reads a predecessor (pred_rows = chunk_len),
  * else -1 (pred_rows = 0).  n_xcd is the number of accelerator dies the
  * workgroups are spread over (8 on MI355X; 1 disables the die-aware order);
- * block_rows is the work-item size (128 or 256; 0 = chunkattn_block_rows()).
+ * block_rows is the work-item size (128, 256 or 384; 0 = chunkattn_block_rows()).
  * Writes at most `cap` records to `items` (may be NULL when cap is 0) and the
  * total count to *n_items.
  */
@@ -348,8 +351,8 @@ int chunkattn_window_plan_debug(int chunk_len, int n_chunks, int heads, int n_xc
 /*
  * The same plan as decoded on the device by the attention kernel's own decode
  * routine: writes n_items * 7 ints to device memory `dev_items` on hip_stream,
- * using the context's die count and work-item size.  For bit-exact tests of
- * the device decode.
+ * using the context's die count and its work-item size for bf16, head_dim-128
+ * calls (chunkattn_ctx_block_rows).  For bit-exact tests of the device decode.
  */
 int chunkattn_plan_device(chunkattn_ctx *ctx, int chunk_len, int n_chunks, int heads,
                           int *dev_items, long long cap, void *hip_stream);

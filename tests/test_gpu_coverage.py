@@ -220,15 +220,17 @@ def test_full_sequence_fingerprint_full_size_bit_exact():
 _ORACLE = {}  # oracle outputs per shape, shared by the two work-item sizes
 
 
-@pytest.mark.parametrize("flags", [pytest.param(ca.FLAG_BLOCK256, id="bm256"),
+@pytest.mark.parametrize("flags", [pytest.param(0, id="default"),
+                                   pytest.param(ca.FLAG_BLOCK256, id="bm256"),
                                    pytest.param(ca.FLAG_BLOCK128, id="bm128")])
 @pytest.mark.parametrize("n,L,H,D", [(5, 800, 48, 64), (4, 900, 32, 128)],
                          ids=["d64", "d128"])
 def test_many_items_whole_output_parity(n, L, H, D, flags):
     """More work items than CUs (960 and 512 at 256 rows per item, 1536 and
-    896 at 128), ragged last query tiles, correlated keys: every output
-    element against the fp64 oracle, the sentinel gone everywhere, and the
-    in-place predecessor form bit-identical to the cache form."""
+    896 at 128, 384 of 384 rows at head_dim 128 with the default context),
+    ragged last query tiles, correlated keys: every output element against the
+    fp64 oracle, the sentinel gone everywhere, and the in-place predecessor
+    form bit-identical to the cache form."""
     say("case many items", (n, L, H, D), flags)
     ctx = ca.create(0, flags)
     q, k, v = synth.queue_inputs(n, L, H, D, seed=400 + D, device=DEV, k_rho=0.9)

@@ -37,7 +37,13 @@ def say(*a):
     sys.stdout.flush()
 
 
-FLAGS = [pytest.param(ca.FLAG_BLOCK256, id="bm256"), pytest.param(ca.FLAG_BLOCK128, id="bm128")]
+# the default context (384-row items for bf16 head_dim 128, 256 otherwise) and
+# the two fixed work-item sizes
+FLAGS = [pytest.param(0, id="default"), pytest.param(ca.FLAG_BLOCK256, id="bm256"),
+         pytest.param(ca.FLAG_BLOCK128, id="bm128")]
+# the two persistent main passes (384- and 256-row items), which share the
+# context's work-queue slots
+PERSISTENT = [pytest.param(0, id="bm384"), pytest.param(ca.FLAG_BLOCK256, id="bm256")]
 
 
 # Finite prefill of outputs that must be overwritten everywhere: above every
@@ -107,14 +113,15 @@ def test_deterministic_and_order_independent_of_stream_state():
     assert torch.equal(a, b)
 
 
-def test_work_queue_slots_reused_across_many_calls():
+@pytest.mark.parametrize("flags", PERSISTENT)
+def test_work_queue_slots_reused_across_many_calls(flags):
     """The 256-row main pass is persistent and takes its items from a work
     queue slot that a clearing kernel zeroes right before it; eager calls cycle
     through 64 slots.  150 back-to-back calls (every slot used twice or more),
     each into an output prefilled with a finite sentinel (NaN would be
     recomputed by the recheck pass), all give the first call's bits: no item is
     skipped or done twice after a slot is reused."""
-    ctx = ca.create(0, ca.FLAG_BLOCK256)
+    ctx = ca.create(0, flags)
     inputs = [synth.queue_inputs(4, 200, 3, 128, seed=s, device=DEV) for s in (21, 22)]
     refs = []
     for q, k, v in inputs:
@@ -132,10 +139,11 @@ def test_work_queue_slots_reused_across_many_calls():
         assert torch.equal(o, refs[i % 2]), f"call {i}"
 
 
-def test_work_queue_two_streams_interleaved():
+@pytest.mark.parametrize("flags", PERSISTENT)
+def test_work_queue_two_streams_interleaved(flags):
     """Calls of one context on two streams, launched alternately without
     synchronisation, use distinct queue slots and match the serial results."""
-    ctx = ca.create(0, ca.FLAG_BLOCK256)
+    ctx = ca.create(0, flags)
     a_in = synth.queue_inputs(8, 700, 5, 128, seed=31, device=DEV)
     b_in = synth.queue_inputs(3, 1000, 4, 64, seed=32, device=DEV)
     ref_a = ca.queue_step(*a_in, None, ctx=ctx)
@@ -154,12 +162,13 @@ def test_work_queue_two_streams_interleaved():
         assert torch.equal(o, ref_a if i % 2 == 0 else ref_b), f"launch {i}"
 
 
-def test_work_queue_under_graph_replay():
+@pytest.mark.parametrize("flags", PERSISTENT)
+def test_work_queue_under_graph_replay(flags):
     """A queue step captured in a HIP graph and replayed several times, with
     eager calls of the same context and synchronisations between replays: the
     captured call has a work-queue slot of its own, cleared by a kernel node
     (no memset node) on every replay, so every replay gives the eager bits."""
-    ctx = ca.create(0, ca.FLAG_BLOCK256)
+    ctx = ca.create(0, flags)
     q, k, v = synth.queue_inputs(4, 600, 3, 128, seed=41, device=DEV)
     ref = ca.queue_step(q, k, v, None, ctx=ctx)
     torch.cuda.synchronize()
@@ -183,13 +192,14 @@ def test_work_queue_under_graph_replay():
         assert torch.equal(eager, ref), f"eager call after replay {rep}"
 
 
-def test_two_graphs_on_two_streams_with_eager_calls():
+@pytest.mark.parametrize("flags", PERSISTENT)
+def test_two_graphs_on_two_streams_with_eager_calls(flags):
     """Two queue steps captured into two graphs, replayed at the same time on
     two streams while eager calls of the same context run on a third, for 70
     rounds (the eager calls wrap round all 64 eager slots): captured calls own
     their slots, so no two launches in flight share one, and every output
     equals its eager reference bit for bit."""
-    ctx = ca.create(0, ca.FLAG_BLOCK256)
+    ctx = ca.create(0, flags)
     ins = [synth.queue_inputs(4, 600, 3, 128, seed=s, device=DEV) for s in (51, 52, 53)]
     refs = [ca.queue_step(*x, None, ctx=ctx) for x in ins]
     torch.cuda.synchronize()
@@ -330,18 +340,21 @@ def test_device_plan_equals_host_plan(flags):
 
 
 def test_block_sizes_agree():
-    """The two launch configurations run different schedules (128-row items:
+    """The three launch configurations run different schedules (128-row items:
     the synchronous one, l summed on the vector ALU; 256-row items: the
-    ping-pong one, no reference maximum and Q pre-scaled), so their sums round in a
-    different order: they agree to a few bf16 rounding steps, well inside the
-    parity bar each of them meets against the oracle."""
+    ping-pong one, no reference maximum and Q pre-scaled; 384-row items: the
+    same on 16x16x32 MFMAs), so their sums round in a different order: they
+    agree to a few bf16 rounding steps, well inside the parity bar each of them
+    meets against the oracle."""
     q, k, v = synth.queue_inputs(5, 700, 3, 128, seed=14, device=DEV, k_rho=0.9)
     cache = synth.build_cache(k, v)
     a = run_queue(q, k, v, cache, flags=ca.FLAG_BLOCK128).float()
     b = run_queue(q, k, v, cache, flags=ca.FLAG_BLOCK256).float()
-    d = (a - b).abs()
-    say("block 128 vs 256: max", d.max().item(), "mean", d.mean().item())
-    assert d.max().item() <= 4e-3 and d.mean().item() <= 2e-4
+    c = run_queue(q, k, v, cache, flags=0).float()
+    for what, x, y in (("128 vs 256", a, b), ("384 vs 256", c, b)):
+        d = (x - y).abs()
+        say("block", what, ": max", d.max().item(), "mean", d.mean().item())
+        assert d.max().item() <= 4e-3 and d.mean().item() <= 2e-4
 
 
 # -------------------------------------------------------------------- full attention

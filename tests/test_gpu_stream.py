@@ -37,7 +37,10 @@ def say(*a):
     sys.stdout.flush()
 
 
-FLAGS = [pytest.param(ca.FLAG_BLOCK256, id="bm256"), pytest.param(ca.FLAG_BLOCK128, id="bm128")]
+# the default context (384-row items for bf16 head_dim 128, 256 otherwise) and
+# the two fixed work-item sizes
+FLAGS = [pytest.param(0, id="default"), pytest.param(ca.FLAG_BLOCK256, id="bm256"),
+         pytest.param(ca.FLAG_BLOCK128, id="bm128")]
 
 
 def ring_inputs(S, L, H, D, seed, dt=torch.bfloat16):

@@ -184,7 +184,7 @@ def _slot_to_work_reference(n, n_xcd, n_first=0):
     return order
 
 
-@pytest.mark.parametrize("bm", [128, 256])
+@pytest.mark.parametrize("bm", [128, 256, 384])
 @pytest.mark.parametrize("L,n,H,xcd", [(128, 4, 2, 8), (6240, 8, 12, 8), (97, 5, 3, 8),
                                        (1, 1, 1, 8), (300, 3, 7, 1), (6240, 8, 40, 8),
                                        (14400, 16, 40, 8), (200, 2, 3, 3)])
@@ -259,11 +259,12 @@ def test_window_plan_order_longest_first():
 
 
 def test_default_block_rows():
-    assert ca.block_rows() in (128, 256)
+    assert ca.block_rows() == 384  # bf16, head_dim 128 calls of a default context
     np.testing.assert_array_equal(ca.plan_debug(300, 3, 2, 8),
                                   ca.plan_debug(300, 3, 2, 8, ca.block_rows()))
     assert ca.plan_debug(300, 3, 2, 8, 128).shape[0] == 3 * 2 * 3
     assert ca.plan_debug(300, 3, 2, 8, 256).shape[0] == 3 * 2 * 2
+    assert ca.plan_debug(800, 3, 2, 8, 384).shape[0] == 3 * 2 * 3
     with pytest.raises(ca.ChunkAttnError):
         ca.plan_debug(300, 3, 2, 8, 96)
 
@@ -294,7 +295,7 @@ def test_slot_to_work_is_a_bijection(n_items, xcd):
     assert sorted(got.tolist()) == list(range(n_items))
 
 
-@pytest.mark.parametrize("bm", [128, 256])
+@pytest.mark.parametrize("bm", [128, 256, 384])
 @pytest.mark.parametrize("L,n,H,xcd", [(97, 5, 3, 8), (128, 4, 2, 8), (300, 3, 7, 8),
                                        (6240, 8, 40, 8), (6240, 8, 12, 8), (1000, 9, 5, 8),
                                        (200, 2, 3, 3), (64, 7, 1, 8), (1, 2, 1, 8)])

@@ -27,7 +27,8 @@ def _gpu():
     yield
 
 
-@pytest.mark.parametrize("flags", [pytest.param(ca.FLAG_BLOCK256, id="bm256"),
+@pytest.mark.parametrize("flags", [pytest.param(0, id="default"),
+                                   pytest.param(ca.FLAG_BLOCK256, id="bm256"),
                                    pytest.param(ca.FLAG_BLOCK128, id="bm128")])
 def test_noalloc_matches_queue_step_two_calls(flags):
     ctx = ca.create(0, flags)

@@ -110,6 +110,12 @@ def main():
             qx = synth.cross_queries(w.n, w.L, w.H, w.D, w.seed, dev, dt)
             kt, vt = synth.text_inputs(w.n_text, w.H, w.D, w.seed, dev, dt)
             ox = torch.empty_like(qx)
+    elif w.kind == "cross":
+        # per-chunk queries over one shared set of text keys/values (batch stride 0)
+        q = synth.cross_queries(w.n, w.L, w.H, w.D, w.seed, dev, dt)
+        k, v = synth.text_inputs(w.lkv, w.H, w.D, w.seed, dev, dt)
+        cache = None
+        out = torch.empty_like(q)
     else:
         q = synth.normal((w.n, w.L, w.H, w.D), w.seed, synth.Q_ID, dev, dt)
         k = synth.normal((w.n, w.lkv, w.H, w.D), w.seed, synth.K_ID, dev, dt)
@@ -233,7 +239,7 @@ def main():
             "chunk_len": w.L,
             "heads": w.H,
             "head_dim": w.D,
-            "lkv": w.lkv if w.kind == "full" else None,
+            "lkv": w.lkv if w.kind in ("full", "cross") else None,
             "window": ("queries of chunks c and c+1; keys of chunks c-1 (cached), c, c+1"
                        if w.kind == "window" else None),
             "kv_cache": ("separate buffer" if cache is not None else
@@ -241,7 +247,7 @@ def main():
                          if w.kind == "stream" else None),
             "ring_slots": w.n + 1 if w.kind == "stream" else None,
             "text_tokens": w.n_text or None,
-            "block_rows": ctx.block_rows,
+            "block_rows": ctx.call_block_rows(w.D, ca.BF16 if w.dtype == "bf16" else ca.F32),
             "flops_per_step": flops_step,
         },
         "queue_steps_per_s": round(1e3 / ms_per_step, 3),

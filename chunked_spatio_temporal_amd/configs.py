@@ -14,7 +14,7 @@ from dataclasses import dataclass, field
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "queue", "window", "stream" or "full"
+    kind: str                 # "queue", "window", "stream", "full" or "cross"
     n: int                    # chunks (queue) or batch (full)
     L: int                    # tokens per chunk (queue) or Lq (full)
     H: int
@@ -47,6 +47,7 @@ class Workload:
                 kv_chunks = 1 + (c >= 1) + (c + 1 < self.n)
                 pairs += q_chunks * kv_chunks
             return 4.0 * pairs * self.L * self.L * self.D * self.H
+        # full attention; cross-attention: every query row over the lkv shared text rows
         return 4.0 * self.n * self.L * self.lkv * self.D * self.H
 
     def nominal_flops(self) -> float:
@@ -86,6 +87,14 @@ WORKLOADS = {
                           note="the 40-head queue as a stream in steady state: 8 live chunks "
                                "in a ring of 9 slots; each step a chunk enters, all 8 are "
                                "processed, the clean head leaves"),
+    "wan14b_h5": Workload("wan14b_h5", "queue", n=8, L=6240, H=5, D=128, dtype="bf16",
+                          k_rho=0.9, seed=2, grid=(4, 30, 52),
+                          note="one GPU's share of the 40-head queue when its heads are split "
+                               "over 8 GPUs: 5 heads"),
+    "cross720p": Workload("cross720p", "cross", n=16, L=14400, H=40, D=128, dtype="bf16",
+                          lkv=512, seed=4, grid=(4, 45, 80),
+                          note="the 720p queue's per-chunk cross-attention alone: 16 x 14400 "
+                               "queries over 512 shared text tokens"),
 }
 
 # The timed workload: the 40-head, 480p-latent queue step.

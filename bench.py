@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block-rows", type=int, default=0, choices=(0, 128, 256, 384),
                     help="query rows per work item (0: library default)")
+    ap.add_argument("--item-blocks", type=int, default=0,
+                    help="384-row query blocks per work item (0: chosen per call, 1..8)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -130,6 +132,9 @@ def main():
     flags = {0: 0, 128: ca.FLAG_BLOCK128, 256: ca.FLAG_BLOCK256,
              384: ca.FLAG_BLOCK384}[args.block_rows]
     ctx = ca.create(0, flags)
+    if args.item_blocks:
+        ctx = ca.Context(0, flags)
+        ctx.set_item_blocks(args.item_blocks)
 
     if w.kind == "stream":
         fifo = ca.Fifo(w.n + 1, w.n)
@@ -201,6 +206,11 @@ def main():
         "launch_ms_min": round(float(launch_ms.min()), 4),
         "launch_ms_p90": round(float(np.percentile(launch_ms, 90)), 4),
     }
+    if args.steps >= 100:
+        # a long run: mean launch time over 10 consecutive segments of the timed
+        # region, to show whether the rate holds as the chip heats up
+        roofline["launch_ms_segments"] = [round(float(s.mean()), 4)
+                                          for s in np.array_split(launch_ms, 10)]
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
@@ -248,6 +258,7 @@ def main():
             "ring_slots": w.n + 1 if w.kind == "stream" else None,
             "text_tokens": w.n_text or None,
             "block_rows": ctx.call_block_rows(w.D, ca.BF16 if w.dtype == "bf16" else ca.F32),
+            "item_blocks": args.item_blocks or "auto",
             "flops_per_step": flops_step,
         },
         "queue_steps_per_s": round(1e3 / ms_per_step, 3),

@@ -51,6 +51,8 @@ def load_library():
     lib.chunkattn_ctx_block_rows.argtypes = [vp]
     lib.chunkattn_ctx_call_block_rows.restype = i32
     lib.chunkattn_ctx_call_block_rows.argtypes = [vp, i32, i32]
+    lib.chunkattn_ctx_set_item_blocks.restype = i32
+    lib.chunkattn_ctx_set_item_blocks.argtypes = [vp, i32]
     lib.chunkattn_create.restype = i32
     lib.chunkattn_create.argtypes = [ctypes.POINTER(vp), i32, ctypes.c_uint]
     lib.chunkattn_destroy.restype = i32
@@ -164,6 +166,10 @@ class Context:
         """Query rows per work item of a call with this head_dim and dtype code."""
         return int(load_library().chunkattn_ctx_call_block_rows(self.handle, int(head_dim),
                                                                 int(dtype)))
+
+    def set_item_blocks(self, blocks: int) -> None:
+        """384-row query blocks per work item (0: chosen per call, 1..8: fixed)."""
+        _check(load_library().chunkattn_ctx_set_item_blocks(self.handle, int(blocks)), self.handle)
 
 
 _contexts: dict[tuple, Context] = {}

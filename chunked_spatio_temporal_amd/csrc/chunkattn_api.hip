@@ -48,6 +48,8 @@ struct chunkattn_ctx {
   // query rows per work item: 128, 256 or 384 (fixed by the flags), or 0 for
   // the default (call_block_rows)
   int block_rows = 0;
+  // 384-row query blocks per work item: 0 = chosen per call (item_blocks)
+  int item_blocks = 0;
   // device, (kQueueSlots + kCaptureSlots) * kQueueWords words
   unsigned long long* queue = nullptr;
   // device address of this device's `scratch` array (noalloc entry point)
@@ -78,6 +80,36 @@ int call_block_rows(const chunkattn_ctx* ctx, int head_dim, int dtype) {
 }
 
 thread_local std::string g_thread_err;
+
+constexpr int kMaxItemBlocks = 8;
+
+// 384-row query blocks per work item of a call with 384-row blocks.  A short
+// key walk (cross-attention over a few hundred text tokens: 8 tiles) costs
+// per item about as much as its tiles (claim, Q load, pipeline fill and
+// drain, final stores); an item of several blocks of one (chunk, head) pays
+// that once.  Chosen: enough blocks for about 48 key tiles per item, while the
+// launch keeps at least 4 items per CU, and one block where an item walks a
+// single key tile.  A context's fixed setting (1..8) overrides the choice.
+int item_blocks(const chunkattn_ctx* ctx, const Plan& p) {
+  if (ctx->item_blocks > 0) return ctx->item_blocks;
+  int min_keys = 0x7fffffff, max_keys = 0;
+  for (int b = 0; b < p.n_batch; ++b) {
+    const int keys =
+        (b >= p.first_pred ? p.lpred : 0) + (b == p.n_batch - 1 ? p.lown_last : p.lown);
+    min_keys = keys < min_keys ? keys : min_keys;
+    max_keys = keys > max_keys ? keys : max_keys;
+  }
+  if (p.n_batch == 0 || min_keys <= chunkattn::kBN) return 1;
+  const int t_max = (max_keys + chunkattn::kBN - 1) / chunkattn::kBN;
+  int g = (48 + t_max - 1) / t_max;
+  g = g < kMaxItemBlocks ? g : kMaxItemBlocks;
+  for (; g > 1; --g) {
+    const Plan q = chunkattn::make_plan(p.n_batch, p.first_pred, p.heads, p.lq, p.lown, p.lpred,
+                                        g * p.bm, p.n_xcd, p.lq_last, p.lown_last);
+    if (q.n_items >= 4 * (int64_t)ctx->n_cu) break;
+  }
+  return g;
+}
 
 int set_err(std::string* sink, int code, const char* fmt, ...) {
   char buf[512];
@@ -302,26 +334,34 @@ hipError_t launch_w(const KernelArgs& a, int n_persist, int head_dim, int dtype,
                                  : launch_t<64, float, W>(a, n_persist, stream);
 }
 
-// The 384-row main pass (48 rows per wave, persistent like the 256-row one),
-// then its recheck (three 128-row items per marked item).
-hipError_t launch_wide(const KernelArgs& a, int n_persist, hipStream_t stream) {
+// The 384-row main pass (48 rows per wave, persistent like the 256-row one):
+// chunk_attn_fwd_wide for items of one block, chunk_attn_fwd_wide_stream for
+// items of several; then the recheck (three 128-row items per marked block).
+// a: the main pass (work items of one or more 384-row blocks); blocks: the same
+// call planned with one block per item, for the recheck.
+hipError_t launch_wide(const KernelArgs& a, const KernelArgs& blocks, int n_persist,
+                       hipStream_t stream) {
   if (!a.queue || n_persist < 1 || a.plan.n_xcd > kQueueWords) return hipErrorInvalidValue;
   hipLaunchKernelGGL(chunkattn::queue_clear, dim3(1), dim3(64), 0, stream, a.queue,
                      a.plan.n_xcd);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chunkattn::chunk_attn_fwd_wide, dim3((unsigned)n_persist), dim3(512),
-                     chunkattn::kPingPongLdsBytes<128>, stream, a);
+  if (a.plan.bm > chunkattn::kWideBlockRows)
+    hipLaunchKernelGGL(chunkattn::chunk_attn_fwd_wide_stream, dim3((unsigned)n_persist),
+                       dim3(512), chunkattn::kPingPongLdsBytes<128>, stream, a);
+  else
+    hipLaunchKernelGGL(chunkattn::chunk_attn_fwd_wide, dim3((unsigned)n_persist), dim3(512),
+                       chunkattn::kPingPongLdsBytes<128>, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chunkattn::chunk_attn_recheck_wide<4>, dim3((unsigned)a.plan.n_items),
-                     dim3(256), chunkattn::kSyncLdsBytes<128>, stream, a);
+  hipLaunchKernelGGL(chunkattn::chunk_attn_recheck_wide<4>, dim3((unsigned)blocks.plan.n_items),
+                     dim3(256), chunkattn::kSyncLdsBytes<128>, stream, blocks);
   return hipGetLastError();
 }
 
-hipError_t launch(const KernelArgs& a, int block_rows, int n_persist, int head_dim, int dtype,
-                  hipStream_t stream) {
-  if (block_rows == 384) return launch_wide(a, n_persist, stream);
+hipError_t launch(const KernelArgs& a, const KernelArgs& blocks, int block_rows, int n_persist,
+                  int head_dim, int dtype, hipStream_t stream) {
+  if (block_rows == 384) return launch_wide(a, blocks, n_persist, stream);
   return block_rows == 128 ? launch_w<4>(a, n_persist, head_dim, dtype, stream)
                            : launch_w<8>(a, n_persist, head_dim, dtype, stream);
 }
@@ -333,10 +373,13 @@ hipError_t allow_wide_lds() {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chunkattn::chunk_attn_fwd_wide),
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)chunkattn::kPingPongLdsBytes<128>);
-  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_acq_rel);
+  for (const void* f : {reinterpret_cast<const void*>(&chunkattn::chunk_attn_fwd_wide),
+                        reinterpret_cast<const void*>(&chunkattn::chunk_attn_fwd_wide_stream)}) {
+    e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)chunkattn::kPingPongLdsBytes<128>);
+    if (e != hipSuccess) return e;
+  }
+  done.fetch_or(bit, std::memory_order_acq_rel);
   return e;
 }
 
@@ -396,9 +439,19 @@ int run(chunkattn_ctx* ctx, const KernelArgs& args, int head_dim, int dtype, voi
     }
     a.queue = ctx->queue + (size_t)slot * kQueueWords;
   }
-  const int n_persist = (int)(a.plan.n_items < ctx->n_cu ? a.plan.n_items : ctx->n_cu);
+  // 384-row blocks: the main pass may take several blocks per work item
+  KernelArgs main = a;
+  if (bm == 384) {
+    const int nb = item_blocks(ctx, a.plan);
+    if (nb > 1) {
+      const Plan& p = a.plan;
+      main.plan = chunkattn::make_plan(p.n_batch, p.first_pred, p.heads, p.lq, p.lown, p.lpred,
+                                       nb * bm, p.n_xcd, p.lq_last, p.lown_last);
+    }
+  }
+  const int n_persist = (int)(main.plan.n_items < ctx->n_cu ? main.plan.n_items : ctx->n_cu);
   const hipError_t e =
-      launch(a, bm, n_persist, head_dim, dtype, static_cast<hipStream_t>(stream));
+      launch(main, a, bm, n_persist, head_dim, dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return set_err(&ctx->err, CHUNKATTN_ELAUNCH, "kernel launch failed: %s",
                    hipGetErrorString(e));
@@ -425,6 +478,16 @@ int chunkattn_ctx_block_rows(const chunkattn_ctx* ctx) {
 
 int chunkattn_ctx_call_block_rows(const chunkattn_ctx* ctx, int head_dim, int dtype) {
   return ctx ? call_block_rows(ctx, head_dim, dtype) : 0;
+}
+
+int chunkattn_ctx_set_item_blocks(chunkattn_ctx* ctx, int blocks) {
+  if (!ctx) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "ctx must be non-NULL");
+  if (blocks < 0 || blocks > kMaxItemBlocks)
+    return set_err(&ctx->err, CHUNKATTN_EINVAL, "item blocks %d outside [0, %d]", blocks,
+                   kMaxItemBlocks);
+  ctx->item_blocks = blocks;
+  ctx->err.clear();
+  return CHUNKATTN_OK;
 }
 
 int chunkattn_create(chunkattn_ctx** out, int device_ordinal, unsigned flags) {

@@ -121,6 +121,17 @@ int chunkattn_ctx_block_rows(const chunkattn_ctx *ctx);
  * head_dim and dtype. */
 int chunkattn_ctx_call_block_rows(const chunkattn_ctx *ctx, int head_dim, int dtype);
 
+/* 384-row query blocks per work item of the context's calls that use 384-row
+ * blocks (bf16, head_dim 128).  A work item of several blocks of one (chunk,
+ * head) walks the chunk's key/value tiles once per block as one continuous
+ * stream, which spares short key walks (cross-attention over text tokens) the
+ * per-item start and finish.  blocks = 0 (the default) chooses per call:
+ * about 48 key tiles per item while the launch keeps at least 4 items per CU;
+ * 1..8 fixes the count.  Results are the same up to fp32 rounding order for
+ * every setting.  CHUNKATTN_EINVAL outside [0, 8].  Not thread-safe against
+ * concurrent calls on the same context. */
+int chunkattn_ctx_set_item_blocks(chunkattn_ctx *ctx, int blocks);
+
 /* Releases a context (NULL is accepted). */
 int chunkattn_destroy(chunkattn_ctx *ctx);
 

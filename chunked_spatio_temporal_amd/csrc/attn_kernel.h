@@ -625,17 +625,31 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
   attn_item_sync<D, T, W, true>(a, it, smem);
 }
 
-// Second pass, launched after chunk_attn_fwd on the same stream with the same
-// grid: recomputes with the running maximum every work item whose first output
-// element carries the overflow marker; the others return after one load.
+// Range recheck after the main pass.  Each thread tests one work item (work
+// index blockIdx.x * blockDim.x + threadIdx.x) for the overflow marker in its
+// first output element; the workgroup then recomputes the items its threads
+// found marked, one after the other, with the running maximum (almost always
+// none).  Grid: ceil(n_items / (64 W)) workgroups.
 template <int D, typename T, int W>
 __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_recheck(KernelArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  const Item it = decode(a.plan, plan_slot_work(a.plan, blockIdx.x));
-  const T first = static_cast<const T*>(a.o)[a.entry(it.b) * a.o_bstride + (int64_t)it.q0 * a.row_stride +
-                                              (int64_t)it.h * D];
-  if (!__builtin_isnan((float)first)) return;
-  attn_item_sync<D, T, W, false>(a, it, smem);
+  __shared__ int marked[W * 64];
+  __shared__ int n_marked;
+  if (threadIdx.x == 0) n_marked = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * blockDim.x;
+  if (base + threadIdx.x < a.plan.n_items) {
+    const Item it = decode(a.plan, base + threadIdx.x);
+    const T first = static_cast<const T*>(a.o)[a.entry(it.b) * a.o_bstride +
+                                                (int64_t)it.q0 * a.row_stride + (int64_t)it.h * D];
+    if (__builtin_isnan((float)first)) marked[atomicAdd(&n_marked, 1)] = (int)threadIdx.x;
+  }
+  __syncthreads();
+  const int n = n_marked;
+  for (int i = 0; i < n; ++i) {
+    attn_item_sync<D, T, W, false>(a, decode(a.plan, base + marked[i]), smem);
+    __syncthreads();
+  }
 }
 
 // Zeroes the n claim words of a work queue (one thread per word), launched on

@@ -319,8 +319,10 @@ hipError_t launch_t(const KernelArgs& a, int n_persist, hipStream_t stream) {
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((chunkattn::chunk_attn_recheck<D, T, W>), grid, dim3(64 * W), kLds, stream,
-                     a);
+  // one thread per work item tests its marker
+  const dim3 check_grid((unsigned)((a.plan.n_items + 64 * W - 1) / (64 * W)));
+  hipLaunchKernelGGL((chunkattn::chunk_attn_recheck<D, T, W>), check_grid, dim3(64 * W), kLds,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -354,8 +356,9 @@ hipError_t launch_wide(const KernelArgs& a, const KernelArgs& blocks, int n_pers
                        chunkattn::kPingPongLdsBytes<128>, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chunkattn::chunk_attn_recheck_wide<4>, dim3((unsigned)blocks.plan.n_items),
-                     dim3(256), chunkattn::kSyncLdsBytes<128>, stream, blocks);
+  hipLaunchKernelGGL(chunkattn::chunk_attn_recheck_wide<4>,
+                     dim3((unsigned)((blocks.plan.n_items + 255) / 256)), dim3(256),
+                     chunkattn::kSyncLdsBytes<128>, stream, blocks);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "chunkattn.h")
 
 OK, EINVAL, EUNSUPPORTED, EDEVICE, ENOMEM, ELAUNCH = range(6)
 BF16, F32 = 0, 1
-FLAG_BLOCK128, FLAG_BLOCK256, FLAG_BLOCK384 = 1, 2, 4
+FLAG_BLOCK128, FLAG_BLOCK256, FLAG_BLOCK384, FLAG_EXACT_SCALE = 1, 2, 4, 8
 PLAN_FIELDS = ("chunk", "head", "q_row0", "q_rows", "pred_chunk", "pred_rows", "own_rows")
 
 
@@ -132,7 +132,8 @@ def block_rows() -> int:
 
 
 class Context:
-    """Owns a chunkattn_ctx bound to one device (flags: FLAG_BLOCK128/256 or 0)."""
+    """Owns a chunkattn_ctx bound to one device (flags: 0 or FLAG_BLOCK128/256/384,
+    optionally | FLAG_EXACT_SCALE)."""
 
     def __init__(self, device: int = 0, flags: int = 0):
         lib = load_library()

@@ -94,12 +94,18 @@ __device__ __forceinline__ void pin(u32x4_t& x) { asm volatile("" : "+v"(x)); }
 // phase of block j+1's first tile (its O is complete once that tile's matrix
 // phase has added P.V of block j's last tile).
 //
+// kExact: Q stays as stored and each key block's scores are multiplied by
+// scale * log2 e in fp32 inside the matrix phase (while the matrix core works
+// on the next key block), instead of rounding scale * log2 e * Q to bf16 once
+// per block: the scores then carry no extra rounding, at the cost of 48
+// multiplies per wave and tile.
+//
 // after_prologue() runs once in every thread, after the prologue's barrier.
 // A wave whose rows of block j left fp32's range sets range_flags[j & 1]
 // (LDS).  Thread 0 marks block j for the recheck in the opening step of block
 // j+2, when every wave is a full phase past block j's stores; the caller
 // marks the item's last two blocks.
-template <int kQB, bool kStream, typename AfterPrologue>
+template <int kQB, bool kStream, bool kExact, typename AfterPrologue>
 __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& it,
                                                unsigned char* smem, int* range_flags,
                                                AfterPrologue&& after_prologue) {
@@ -202,7 +208,9 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
     }
   };
   // scaled by scale * log2 e (nearest-even): S^T comes out in the log2 domain
+  // (exact-scale items leave Q as stored and scale S instead)
   auto scale_q = [&]() __attribute__((always_inline)) {
+    if constexpr (kExact) return;
 #pragma unroll
     for (int q3 = 0; q3 < kQB; ++q3)
 #pragma unroll
@@ -367,6 +375,12 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
       fr[0] = read(i0);
       fr[1] = read(i0 + 1);
     }
+    auto scale_s = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q3 = 0; q3 < kQB; ++q3)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sacc[q3][kb][e] *= a.scale_log2;
+    };
     auto one_step = [&](int i) __attribute__((always_inline)) {
       if (i + 2 < i1) fr[(i - i0 + 2) % 3] = read(i + 2);
       const u32x4_t f = fr[(i - i0) % 3];
@@ -384,6 +398,9 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
           sacc[q3][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8_t, f), __builtin_bit_cast(bf16x8_t, qf[q3][ks]),
               ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : sacc[q3][kb], 0, 0, 0);
+        // exact scale: S of key block kb-1 is complete; into the log2 domain
+        // while the matrix core works on block kb
+        if (kExact && ks == 2 && kb >= 1) scale_s(kb - 1);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -394,6 +411,7 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = kStepsPV > i0 ? kStepsPV : i0; i < i1; ++i) one_step(i);
+    if constexpr (kExact && kQK) scale_s(kKB - 1);
   };
 
   // Softmax phase of tile t: numerators 2^S into pk and l (with a mask, keys
@@ -622,7 +640,7 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
 // three, two or one query blocks per wave by the item's rows; kStream = true:
 // work items of several 384-row blocks of one (chunk, head) (plan.bm a
 // multiple of 384), every block with three query blocks per wave.
-template <bool kStream>
+template <bool kStream, bool kExact>
 __device__ __forceinline__ void wide_persistent(const KernelArgs& a, unsigned char* smem) {
   __shared__ long long next_item;  // >= 0 item, -1 none left, -2 claim again
   __shared__ int used_up;          // thread 0: dies (from our own on) found empty
@@ -675,11 +693,11 @@ __device__ __forceinline__ void wide_persistent(const KernelArgs& a, unsigned ch
     };
     const Item it = decode(a.plan, w);
     if (kStream || it.q_rows > 2 * 16 * kWideWaves)
-      attn_item_wide<3, kStream>(a, it, smem, range_flags, after_prologue);
+      attn_item_wide<3, kStream, kExact>(a, it, smem, range_flags, after_prologue);
     else if (it.q_rows > 16 * kWideWaves)
-      attn_item_wide<2, false>(a, it, smem, range_flags, after_prologue);
+      attn_item_wide<2, false, kExact>(a, it, smem, range_flags, after_prologue);
     else
-      attn_item_wide<1, false>(a, it, smem, range_flags, after_prologue);
+      attn_item_wide<1, false, kExact>(a, it, smem, range_flags, after_prologue);
     wg_barrier();
     if (threadIdx.x == 0) {
       // the item's last two blocks (the item marked the ones before); each
@@ -709,12 +727,24 @@ __device__ __forceinline__ void wide_persistent(const KernelArgs& a, unsigned ch
 
 __global__ __launch_bounds__(512, 1) void chunk_attn_fwd_wide(KernelArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  wide_persistent<false>(a, smem);
+  wide_persistent<false, false>(a, smem);
 }
 
 __global__ __launch_bounds__(512, 1) void chunk_attn_fwd_wide_stream(KernelArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  wide_persistent<true>(a, smem);
+  wide_persistent<true, false>(a, smem);
+}
+
+// The same two passes with the scale applied to S in fp32 (exact-scale
+// contexts).
+__global__ __launch_bounds__(512, 1) void chunk_attn_fwd_wide_exact(KernelArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  wide_persistent<false, true>(a, smem);
+}
+
+__global__ __launch_bounds__(512, 1) void chunk_attn_fwd_wide_stream_exact(KernelArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  wide_persistent<true, true>(a, smem);
 }
 
 // Recheck of 384-row blocks, planned one block per item: each thread tests

@@ -50,6 +50,8 @@ struct chunkattn_ctx {
   int block_rows = 0;
   // 384-row query blocks per work item: 0 = chosen per call (item_blocks)
   int item_blocks = 0;
+  // scores scaled in fp32 (CHUNKATTN_FLAG_EXACT_SCALE)
+  bool exact_scale = false;
   // device, (kQueueSlots + kCaptureSlots) * kQueueWords words
   unsigned long long* queue = nullptr;
   // device address of this device's `scratch` array (noalloc entry point)
@@ -76,7 +78,8 @@ bool wide_supported(int head_dim, int dtype) { return head_dim == 128 && dtype =
 // for every other call.
 int call_block_rows(const chunkattn_ctx* ctx, int head_dim, int dtype) {
   if (ctx->block_rows == 128 || ctx->block_rows == 256) return ctx->block_rows;
-  return wide_supported(head_dim, dtype) ? 384 : 256;
+  // exact-scale contexts: the 256-row pass rounds the scaled Q to bf16
+  return wide_supported(head_dim, dtype) ? 384 : ctx->exact_scale ? 128 : 256;
 }
 
 thread_local std::string g_thread_err;
@@ -341,19 +344,19 @@ hipError_t launch_w(const KernelArgs& a, int n_persist, int head_dim, int dtype,
 // items of several; then the recheck (three 128-row items per marked block).
 // a: the main pass (work items of one or more 384-row blocks); blocks: the same
 // call planned with one block per item, for the recheck.
-hipError_t launch_wide(const KernelArgs& a, const KernelArgs& blocks, int n_persist,
+hipError_t launch_wide(const KernelArgs& a, const KernelArgs& blocks, int n_persist, bool exact,
                        hipStream_t stream) {
   if (!a.queue || n_persist < 1 || a.plan.n_xcd > kQueueWords) return hipErrorInvalidValue;
   hipLaunchKernelGGL(chunkattn::queue_clear, dim3(1), dim3(64), 0, stream, a.queue,
                      a.plan.n_xcd);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.plan.bm > chunkattn::kWideBlockRows)
-    hipLaunchKernelGGL(chunkattn::chunk_attn_fwd_wide_stream, dim3((unsigned)n_persist),
-                       dim3(512), chunkattn::kPingPongLdsBytes<128>, stream, a);
-  else
-    hipLaunchKernelGGL(chunkattn::chunk_attn_fwd_wide, dim3((unsigned)n_persist), dim3(512),
-                       chunkattn::kPingPongLdsBytes<128>, stream, a);
+  const bool multi = a.plan.bm > chunkattn::kWideBlockRows;
+  auto kernel = multi ? (exact ? chunkattn::chunk_attn_fwd_wide_stream_exact
+                               : chunkattn::chunk_attn_fwd_wide_stream)
+                      : (exact ? chunkattn::chunk_attn_fwd_wide_exact : chunkattn::chunk_attn_fwd_wide);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)n_persist), dim3(512),
+                     chunkattn::kPingPongLdsBytes<128>, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(chunkattn::chunk_attn_recheck_wide<4>,
@@ -363,8 +366,8 @@ hipError_t launch_wide(const KernelArgs& a, const KernelArgs& blocks, int n_pers
 }
 
 hipError_t launch(const KernelArgs& a, const KernelArgs& blocks, int block_rows, int n_persist,
-                  int head_dim, int dtype, hipStream_t stream) {
-  if (block_rows == 384) return launch_wide(a, blocks, n_persist, stream);
+                  int head_dim, int dtype, bool exact, hipStream_t stream) {
+  if (block_rows == 384) return launch_wide(a, blocks, n_persist, exact, stream);
   return block_rows == 128 ? launch_w<4>(a, n_persist, head_dim, dtype, stream)
                            : launch_w<8>(a, n_persist, head_dim, dtype, stream);
 }
@@ -377,7 +380,9 @@ hipError_t allow_wide_lds() {
   const uint64_t bit = 1ull << (dev & 63);
   if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
   for (const void* f : {reinterpret_cast<const void*>(&chunkattn::chunk_attn_fwd_wide),
-                        reinterpret_cast<const void*>(&chunkattn::chunk_attn_fwd_wide_stream)}) {
+                        reinterpret_cast<const void*>(&chunkattn::chunk_attn_fwd_wide_stream),
+                        reinterpret_cast<const void*>(&chunkattn::chunk_attn_fwd_wide_exact),
+                        reinterpret_cast<const void*>(&chunkattn::chunk_attn_fwd_wide_stream_exact)}) {
     e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)chunkattn::kPingPongLdsBytes<128>);
     if (e != hipSuccess) return e;
@@ -454,7 +459,8 @@ int run(chunkattn_ctx* ctx, const KernelArgs& args, int head_dim, int dtype, voi
   }
   const int n_persist = (int)(main.plan.n_items < ctx->n_cu ? main.plan.n_items : ctx->n_cu);
   const hipError_t e =
-      launch(main, a, bm, n_persist, head_dim, dtype, static_cast<hipStream_t>(stream));
+      launch(main, a, bm, n_persist, head_dim, dtype, ctx->exact_scale,
+             static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return set_err(&ctx->err, CHUNKATTN_ELAUNCH, "kernel launch failed: %s",
                    hipGetErrorString(e));
@@ -496,8 +502,11 @@ int chunkattn_ctx_set_item_blocks(chunkattn_ctx* ctx, int blocks) {
 int chunkattn_create(chunkattn_ctx** out, int device_ordinal, unsigned flags) {
   if (!out) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "out must be non-NULL");
   *out = nullptr;
-  const unsigned known = CHUNKATTN_FLAG_BLOCK128 | CHUNKATTN_FLAG_BLOCK256 | CHUNKATTN_FLAG_BLOCK384;
-  if ((flags & ~known) != 0 || (flags & (flags - 1)) != 0)
+  const unsigned sizes = CHUNKATTN_FLAG_BLOCK128 | CHUNKATTN_FLAG_BLOCK256 | CHUNKATTN_FLAG_BLOCK384;
+  const unsigned size = flags & sizes;
+  const bool exact = (flags & CHUNKATTN_FLAG_EXACT_SCALE) != 0;
+  if ((flags & ~(sizes | CHUNKATTN_FLAG_EXACT_SCALE)) != 0 || (size & (size - 1)) != 0 ||
+      (exact && size == CHUNKATTN_FLAG_BLOCK256))
     return set_err(&g_thread_err, CHUNKATTN_EINVAL, "unknown or conflicting flags 0x%x", flags);
   int count = 0;
   if (hipGetDeviceCount(&count) != hipSuccess || device_ordinal < 0 || device_ordinal >= count)
@@ -513,10 +522,11 @@ int chunkattn_create(chunkattn_ctx** out, int device_ordinal, unsigned flags) {
   chunkattn_ctx* ctx = new (std::nothrow) chunkattn_ctx();
   if (!ctx) return set_err(&g_thread_err, CHUNKATTN_ENOMEM, "context allocation failed");
   ctx->device = device_ordinal;
-  ctx->block_rows = flags == CHUNKATTN_FLAG_BLOCK128   ? 128
-                    : flags == CHUNKATTN_FLAG_BLOCK256 ? 256
-                    : flags == CHUNKATTN_FLAG_BLOCK384 ? 384
-                                                       : 0;
+  ctx->block_rows = size == CHUNKATTN_FLAG_BLOCK128   ? 128
+                    : size == CHUNKATTN_FLAG_BLOCK256 ? 256
+                    : size == CHUNKATTN_FLAG_BLOCK384 ? 384
+                                                      : 0;
+  ctx->exact_scale = exact;
   ctx->n_cu = prop.multiProcessorCount;
   ctx->arch = prop.gcnArchName;
   int xcc = 0;

@@ -97,6 +97,16 @@ typedef enum {
 #define CHUNKATTN_FLAG_BLOCK256 2u /* 256 rows, 8 waves of 32 rows, one workgroup per CU */
 #define CHUNKATTN_FLAG_BLOCK384 4u /* 384 rows, 8 waves of 48 rows, one workgroup per CU,
                                       for bf16 head_dim 128 (256 rows otherwise) */
+/* Exact scale (may be or-ed with CHUNKATTN_FLAG_BLOCK384 or BLOCK128).  The
+ * default 384- and 256-row passes round scale * log2(e) * Q to bf16 once per
+ * work item, which adds a relative error of up to 2^-9 to every score term:
+ * harmless for near-uniform softmax rows, but it grows with the spread of the
+ * logits (natural-logit standard deviation 5 gives max-abs output errors near
+ * 2e-2 against 1e-2 for exact scaling).  With this flag the scores are scaled
+ * in fp32 instead: 384-row items multiply S by scale * log2(e) (about 6% more
+ * time), calls without the 384-row kernel use 128-row items (which always
+ * scale in fp32).  CHUNKATTN_EINVAL together with CHUNKATTN_FLAG_BLOCK256. */
+#define CHUNKATTN_FLAG_EXACT_SCALE 8u
 
 /* Query rows per work item of a bf16, head_dim-128 call on a context created
  * with flags = 0 (384). */
@@ -106,8 +116,9 @@ int chunkattn_block_rows(void);
  * Creates a context bound to HIP device `device_ordinal`.  Fails with
  * CHUNKATTN_EUNSUPPORTED unless the device is gfx950, CHUNKATTN_EDEVICE if the
  * ordinal is invalid.  `flags` is 0 (library default work-item size) or one of
- * CHUNKATTN_FLAG_BLOCK128 / CHUNKATTN_FLAG_BLOCK256; results do not depend on
- * it beyond fp32 rounding order.  On success *out owns the context; release it
+ * CHUNKATTN_FLAG_BLOCK128 / CHUNKATTN_FLAG_BLOCK256 / CHUNKATTN_FLAG_BLOCK384,
+ * optionally or-ed with CHUNKATTN_FLAG_EXACT_SCALE; results do not depend on
+ * the work-item size beyond fp32 rounding order.  On success *out owns the context; release it
  * with chunkattn_destroy.  CHUNKATTN_EDEVICE also reports a failed allocation
  * of the work queue (256-row contexts).
  */

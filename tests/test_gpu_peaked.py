@@ -1,0 +1,195 @@
+"""Peaked softmax rows: queries scaled so that the natural logits q.k * scale
+have standard deviation 2 to 10 (a few keys carry most of each row's weight),
+and rows whose scores leave fp32's range without a maximum.  Every output
+element is compared with the fp64 oracle (DualParal write-up, section 三: each
+chunk attends over the cached K/V of its predecessor and its own).
+
+Two arithmetic modes of the 384-row pass:
+* default: scale * log2(e) * Q is rounded to bf16 once per work item, which
+  adds up to 2^-9 relative error to every term of a score;
+* exact scale (CHUNKATTN_FLAG_EXACT_SCALE): S is scaled in fp32.
+Both round the numerators P and the output to bf16.  Where a bf16 kernel can
+meet the fixed bar (max-abs 1e-2, mean-abs 1e-3) the test applies it; beyond
+that, every element must lie within the error bound that these roundings
+imply (parity_util.rounding_bound), and the mean stays within the bar.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunked_spatio_temporal_amd import chunkattn as ca
+from chunked_spatio_temporal_amd import synth
+from parity_util import (MEAN_ABS, REL_L2, assert_parity, assert_within_bound, error_stats,
+                         rounding_bound, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+SENTINEL = 2.0 ** 100
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ca.load_library()
+    yield
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def peaked_queue_inputs(n, L, H, D, std, seed, hot_rows=None, hot_std=None):
+    """Q = std * N(0, 1) (natural-logit std `std` against unit K), optionally
+    with some rows at hot_std; K, V ~ N(0, 1)."""
+    q = synth.normal((n, L, H, D), seed, synth.Q_ID, DEV, torch.float32) * std
+    if hot_rows is not None:
+        q[:, hot_rows] *= hot_std / std
+    q = q.to(torch.bfloat16)
+    k = synth.normal((n, L, H, D), seed, synth.K_ID, DEV)
+    v = synth.normal((n, L, H, D), seed, synth.V_ID, DEV)
+    return q, k, v
+
+
+def bound_for_queue(q, k, v, ref, scale, q_rounded):
+    """rounding_bound for every row of a queue step (chunk c's keys: the cache
+    of chunk c-1, then its own)."""
+    n, L, H, D = q.shape
+    Q = to_f64(q)
+    K = to_f64(k)
+    V = to_f64(v)
+    c = np.float32(scale / np.log(2.0))
+    out = np.empty_like(ref)
+    for ch in range(n):
+        for h in range(H):
+            keys = np.concatenate([K[ch - 1, :, h], K[ch, :, h]]) if ch >= 1 else K[ch, :, h]
+            vals = np.concatenate([V[ch - 1, :, h], V[ch, :, h]]) if ch >= 1 else V[ch, :, h]
+            dS = None
+            if q_rounded:
+                # scores from bf16(c q): |dS_j| <= 2^-9 sum_i |c q_i k_ji|
+                dS = 2.0 ** -9 * (np.abs(Q[ch, :, h] * c) @ np.abs(keys).T).max(1)
+            out[ch, :, h] = rounding_bound(ref[ch, :, h], np.abs(vals).max(0), dS)
+    return out
+
+
+N, L, H, D = 2, 700, 2, 128
+
+
+def run(ctx, q, k, v, cache):
+    out = torch.full_like(q, SENTINEL)
+    ca.queue_step(q, k, v, cache, out=out, ctx=ctx)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_exact_scale_flag_combinations():
+    ca.Context(0, ca.FLAG_EXACT_SCALE)
+    ca.Context(0, ca.FLAG_EXACT_SCALE | ca.FLAG_BLOCK384)
+    ca.Context(0, ca.FLAG_EXACT_SCALE | ca.FLAG_BLOCK128)
+    with pytest.raises(ca.ChunkAttnError):
+        ca.Context(0, ca.FLAG_EXACT_SCALE | ca.FLAG_BLOCK256)
+    with pytest.raises(ca.ChunkAttnError):
+        ca.Context(0, ca.FLAG_BLOCK128 | ca.FLAG_BLOCK384)
+
+
+@pytest.mark.parametrize("std", [2, 3, 5, 10])
+def test_exact_scale_peaked(std):
+    """Exact scale: the fixed bar up to std 3; at 5 and 10 the P rounding alone
+    reaches ~1e-2, so the per-element rounding bound applies (and the mean bar)."""
+    say("case exact peaked", std)
+    q, k, v = peaked_queue_inputs(N, L, H, D, std, 700 + std)
+    cache = synth.build_cache(k, v)
+    out = run(ca.create(0, ca.FLAG_EXACT_SCALE), q, k, v, cache)
+    ref = oracle.queue_step(q, k, v, cache)
+    got = to_f64(out)
+    if std <= 3:
+        s = assert_parity(got, ref, f"exact std {std}")
+    else:
+        s = assert_within_bound(got, ref, bound_for_queue(q, k, v, ref, D ** -0.5, False),
+                                f"exact std {std}")
+        assert s["mean_abs"] <= MEAN_ABS, s
+    say("stats", s)
+
+
+@pytest.mark.parametrize("std", [2, 3, 5, 10])
+def test_default_scale_peaked(std):
+    """Default (Q scaled and rounded to bf16): the fixed bar at std 2; beyond,
+    the bound that adds the score error of the rounded Q (the mean error grows
+    past 1e-3 from std 3 on; the relative L2 error stays under 1e-2)."""
+    say("case default peaked", std)
+    q, k, v = peaked_queue_inputs(N, L, H, D, std, 700 + std)
+    cache = synth.build_cache(k, v)
+    out = run(ca.create(0), q, k, v, cache)
+    ref = oracle.queue_step(q, k, v, cache)
+    got = to_f64(out)
+    if std <= 2:
+        s = assert_parity(got, ref, f"default std {std}")
+    else:
+        s = assert_within_bound(got, ref, bound_for_queue(q, k, v, ref, D ** -0.5, True),
+                                f"default std {std}")
+        assert error_stats(got, ref)["rel_l2"] <= REL_L2
+    say("stats", s)
+
+
+@pytest.mark.parametrize("flags", [pytest.param(0, id="default"),
+                                   pytest.param(ca.FLAG_EXACT_SCALE, id="exact")])
+def test_rows_beyond_fp32_range_are_rechecked(flags):
+    """Rows 0-99 and 500-549 of every chunk at natural-logit std 40 (maxima
+    near 150, past 2^128 without a maximum): their work items are recomputed by
+    the running-maximum pass, which scales S in fp32; the rest stay at std 2.
+    Every element within the rounding bound, the mean within the bar."""
+    hot = list(range(0, 100)) + list(range(500, 550))
+    say("case overflow rows", flags)
+    q, k, v = peaked_queue_inputs(N, L, H, D, 2, 777, hot_rows=hot, hot_std=40)
+    cache = synth.build_cache(k, v)
+    out = run(ca.create(0, flags), q, k, v, cache)
+    ref = oracle.queue_step(q, k, v, cache)
+    got = to_f64(out)
+    # items of the hot rows are recomputed exactly; the others carry the mode's rounding
+    b = bound_for_queue(q, k, v, ref, D ** -0.5, flags == 0)
+    s = assert_within_bound(got, ref, b, "overflow rows")
+    assert s["mean_abs"] <= MEAN_ABS, s
+    say("stats", s)
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_exact_scale_cross_attention_item_blocks(G):
+    """Exact scale with multi-block work items: 2 x 1600 queries (std 5) over
+    512 shared text rows; G = 4 must equal G = 1 bit for bit, both within the
+    rounding bound of the oracle."""
+    B, lq, T = 2, 1600, 512
+    q = (synth.cross_queries(B, lq, H, D, 901, DEV, torch.float32) * 5).to(torch.bfloat16)
+    kt, vt = synth.text_inputs(T, H, D, 901, DEV, torch.bfloat16)
+    outs = []
+    for g in (1, G):
+        c = ca.Context(0, ca.FLAG_EXACT_SCALE)
+        c.set_item_blocks(g)
+        o = torch.full_like(q, SENTINEL)
+        ca.full(q, kt, vt, out=o, ctx=c)
+        torch.cuda.synchronize()
+        outs.append(o)
+    assert torch.equal(outs[0], outs[1])
+    ref = oracle.full(q, kt, vt)
+    vmax = np.abs(to_f64(vt)[0]).max(0)  # [H, D]
+    b = np.empty_like(ref)
+    for i in range(B):
+        for h in range(H):
+            b[i, :, h] = rounding_bound(ref[i, :, h], vmax[h])
+    s = assert_within_bound(to_f64(outs[1]), ref, b, f"exact cross G={G}")
+    say("stats", s)
+
+
+def test_exact_scale_head_dim_64_uses_exact_items():
+    """head_dim 64 has no 384-row kernel: an exact-scale context runs it on
+    128-row items (scaled in fp32); std 3 meets the fixed bar."""
+    q, k, v = peaked_queue_inputs(N, 300, H, 64, 3, 990)
+    cache = synth.build_cache(k, v)
+    ctx = ca.create(0, ca.FLAG_EXACT_SCALE)
+    assert ctx.call_block_rows(64, ca.BF16) == 128
+    out = run(ctx, q, k, v, cache)
+    assert_parity(to_f64(out), oracle.queue_step(q, k, v, cache), "exact d64")

@@ -62,6 +62,11 @@ def parse():
                     help="query rows per work item (0: library default)")
     ap.add_argument("--item-blocks", type=int, default=0,
                     help="384-row query blocks per work item (0: chosen per call, 1..8)")
+    ap.add_argument("--peaked", type=float, default=0.0,
+                    help="scale Q so that the natural logits have this standard deviation "
+                         "(queue workloads; 0: unit-scale inputs)")
+    ap.add_argument("--exact-scale", action="store_true",
+                    help="context with the exact-scale flag (scores scaled in fp32)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -103,6 +108,8 @@ def main():
     elif w.kind in ("queue", "window"):
         q, k, v = synth.queue_inputs(w.n, w.L, w.H, w.D, w.seed, device=dev, dtype=dt,
                                      k_rho=w.k_rho, v_rho=w.v_rho)
+        if args.peaked:
+            q = (q.float() * args.peaked).to(dt)
         cache = synth.build_cache(k, v)
         if w.kind == "queue":
             out = torch.empty_like(q)
@@ -131,6 +138,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
     flags = {0: 0, 128: ca.FLAG_BLOCK128, 256: ca.FLAG_BLOCK256,
              384: ca.FLAG_BLOCK384}[args.block_rows]
+    if args.exact_scale:
+        flags |= ca.FLAG_EXACT_SCALE
     ctx = ca.create(0, flags)
     if args.item_blocks:
         ctx = ca.Context(0, flags)
@@ -259,6 +268,9 @@ def main():
             "text_tokens": w.n_text or None,
             "block_rows": ctx.call_block_rows(w.D, ca.BF16 if w.dtype == "bf16" else ca.F32),
             "item_blocks": args.item_blocks or "auto",
+            "logit_std": args.peaked or 1.0,
+            "scale_mode": "exact (S scaled in fp32)" if args.exact_scale else
+                          "default (scaled Q rounded to bf16)",
             "flops_per_step": flops_step,
         },
         "queue_steps_per_s": round(1e3 / ms_per_step, 3),
@@ -266,6 +278,9 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+
+    if args.peaked and w.kind == "queue":
+        record["recheck"] = recheck_share(w, q, k, v, cache)
 
     if not args.no_cpu_baseline:
         if w.kind == "stream":
@@ -360,6 +375,31 @@ def bench_noise(args, w):
                                   "cores": 1, "kind": "oracle",
                                   "sample": f"{count} chained chunk inits in {dt_cpu:.1f} s"}
     print(json.dumps(record), flush=True)
+
+
+def recheck_share(w, q, k, v, cache):
+    """Share of 384-row work items that the range recheck recomputes: items
+    with a row whose sum l = sum_j 2^(S_j) (S in log2 units) leaves
+    [2^-64, 2^128), computed in fp32 from the same inputs (outside the timed
+    region)."""
+    import math
+
+    import torch
+    c = w.scale / math.log(2.0)
+    L, bm = w.L, 384
+    n_items = marked = 0
+    for ch in range(w.n):
+        for h in range(w.H):
+            # cache[ch, 0] holds the K of chunk ch - 1
+            keys = k[ch, :, h] if ch == 0 else torch.cat([cache[ch, 0, :, h], k[ch, :, h]])
+            s = (q[ch, :, h].float() @ keys.float().T) * c
+            l2 = torch.logsumexp(s * math.log(2.0), dim=1) / math.log(2.0)
+            bad = ((l2 >= 128) | (l2 < -64)).cpu()
+            for t in range(0, L, bm):
+                n_items += 1
+                marked += int(bad[t:t + bm].any())
+    return {"items": n_items, "items_rechecked": marked,
+            "share": round(marked / max(n_items, 1), 5)}
 
 
 def cpu_baseline(w, q, k, v, cache, seconds):

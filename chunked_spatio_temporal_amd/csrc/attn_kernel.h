@@ -625,30 +625,38 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_fwd(KernelArgs a) {
   attn_item_sync<D, T, W, true>(a, it, smem);
 }
 
-// Range recheck after the main pass.  Each thread tests one work item (work
-// index blockIdx.x * blockDim.x + threadIdx.x) for the overflow marker in its
-// first output element; the workgroup then recomputes the items its threads
-// found marked, one after the other, with the running maximum (almost always
-// none).  Grid: ceil(n_items / (64 W)) workgroups.
+// Range recheck after the main pass.  Workgroup g takes a contiguous share of
+// the work items (ceil(n_items / gridDim.x) of them), tests their overflow
+// markers (the first output element of each item) one item per thread, and
+// recomputes the items it found marked, one after the other, with the running
+// maximum.  With two workgroups per CU the test costs one load per item,
+// spread over the chip, and a launch whose items all overflowed still
+// recomputes them on every CU.
 template <int D, typename T, int W>
 __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_recheck(KernelArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __shared__ int marked[W * 64];
   __shared__ int n_marked;
-  if (threadIdx.x == 0) n_marked = 0;
-  __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * blockDim.x;
-  if (base + threadIdx.x < a.plan.n_items) {
-    const Item it = decode(a.plan, base + threadIdx.x);
-    const T first = static_cast<const T*>(a.o)[a.entry(it.b) * a.o_bstride +
-                                                (int64_t)it.q0 * a.row_stride + (int64_t)it.h * D];
-    if (__builtin_isnan((float)first)) marked[atomicAdd(&n_marked, 1)] = (int)threadIdx.x;
-  }
-  __syncthreads();
-  const int n = n_marked;
-  for (int i = 0; i < n; ++i) {
-    attn_item_sync<D, T, W, false>(a, decode(a.plan, base + marked[i]), smem);
+  const int64_t n = a.plan.n_items;
+  const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = lo + per < n ? lo + per : n;
+  for (int64_t base = lo; base < hi; base += blockDim.x) {
+    if (threadIdx.x == 0) n_marked = 0;
     __syncthreads();
+    if (base + threadIdx.x < hi) {
+      const Item it = decode(a.plan, base + threadIdx.x);
+      const T first = static_cast<const T*>(a.o)[a.entry(it.b) * a.o_bstride +
+                                                  (int64_t)it.q0 * a.row_stride +
+                                                  (int64_t)it.h * D];
+      if (__builtin_isnan((float)first)) marked[atomicAdd(&n_marked, 1)] = (int)threadIdx.x;
+    }
+    __syncthreads();
+    const int m = n_marked;
+    for (int i = 0; i < m; ++i) {
+      attn_item_sync<D, T, W, false>(a, decode(a.plan, base + marked[i]), smem);
+      __syncthreads();
+    }
   }
 }
 

@@ -747,37 +747,41 @@ __global__ __launch_bounds__(512, 1) void chunk_attn_fwd_wide_stream_exact(Kerne
   wide_persistent<true, true>(a, smem);
 }
 
-// Recheck of 384-row blocks, planned one block per item: each thread tests
-// one block (work index blockIdx.x * blockDim.x + threadIdx.x) for the
-// overflow marker in its first output element; the workgroup then recomputes
-// the marked blocks it found, each as three 128-row items on the
-// running-maximum schedule.  Grid: ceil(n_items / (64 W)) workgroups.
+// Recheck of 384-row blocks, planned one block per item, organised as
+// chunk_attn_recheck: each workgroup tests its share of the blocks (one per
+// thread) and recomputes the marked ones, each as three 128-row items on the
+// running-maximum schedule.
 template <int W>
 __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_recheck_wide(KernelArgs a) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __shared__ int marked[W * 64];
   __shared__ int n_marked;
-  if (threadIdx.x == 0) n_marked = 0;
-  __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * blockDim.x;
-  if (base + threadIdx.x < a.plan.n_items) {
-    const Item it = decode(a.plan, base + threadIdx.x);
-    const __bf16 first = static_cast<const __bf16*>(a.o)[a.entry(it.b) * a.o_bstride +
-                                                        (int64_t)it.q0 * a.row_stride +
-                                                        (int64_t)it.h * 128];
-    if (__builtin_isnan((float)first)) marked[atomicAdd(&n_marked, 1)] = (int)threadIdx.x;
-  }
-  __syncthreads();
-  const int n = n_marked;
-  for (int i = 0; i < n; ++i) {
-    const Item it = decode(a.plan, base + marked[i]);
-    for (int sub = 0; sub * 32 * W < it.q_rows; ++sub) {
-      Item s = it;
-      s.q0 = it.q0 + sub * 32 * W;
-      const int left = it.q_rows - sub * 32 * W;
-      s.q_rows = left < 32 * W ? left : 32 * W;
-      attn_item_sync<128, __bf16, W, false>(a, s, smem);
-      __syncthreads();
+  const int64_t n = a.plan.n_items;
+  const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = lo + per < n ? lo + per : n;
+  for (int64_t base = lo; base < hi; base += blockDim.x) {
+    if (threadIdx.x == 0) n_marked = 0;
+    __syncthreads();
+    if (base + threadIdx.x < hi) {
+      const Item it = decode(a.plan, base + threadIdx.x);
+      const __bf16 first = static_cast<const __bf16*>(a.o)[a.entry(it.b) * a.o_bstride +
+                                                          (int64_t)it.q0 * a.row_stride +
+                                                          (int64_t)it.h * 128];
+      if (__builtin_isnan((float)first)) marked[atomicAdd(&n_marked, 1)] = (int)threadIdx.x;
+    }
+    __syncthreads();
+    const int m = n_marked;
+    for (int i = 0; i < m; ++i) {
+      const Item it = decode(a.plan, base + marked[i]);
+      for (int sub = 0; sub * 32 * W < it.q_rows; ++sub) {
+        Item s = it;
+        s.q0 = it.q0 + sub * 32 * W;
+        const int left = it.q_rows - sub * 32 * W;
+        s.q_rows = left < 32 * W ? left : 32 * W;
+        attn_item_sync<128, __bf16, W, false>(a, s, smem);
+        __syncthreads();
+      }
     }
   }
 }

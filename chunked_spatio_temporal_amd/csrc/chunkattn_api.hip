@@ -301,8 +301,15 @@ hipError_t allow_pingpong_lds() {
 // the same stream.
 // W = 8: the main pass is persistent, n_persist workgroups (one per CU) share
 // the work items through the work queue a.queue.
+// Recheck grid: two workgroups per CU, each testing a contiguous share of the
+// work items (fewer if there are fewer items).
+dim3 recheck_grid(int64_t n_items, int n_cu) {
+  const int64_t g = 2 * (int64_t)(n_cu > 0 ? n_cu : 1);
+  return dim3((unsigned)(n_items < g ? (n_items > 0 ? n_items : 1) : g));
+}
+
 template <int D, typename T, int W>
-hipError_t launch_t(const KernelArgs& a, int n_persist, hipStream_t stream) {
+hipError_t launch_t(const KernelArgs& a, int n_persist, int n_cu, hipStream_t stream) {
   const dim3 grid((unsigned)a.plan.n_items);
   constexpr uint32_t kLds = chunkattn::kSyncLdsBytes<D>;
   if constexpr (W == 8) {
@@ -322,21 +329,20 @@ hipError_t launch_t(const KernelArgs& a, int n_persist, hipStream_t stream) {
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // one thread per work item tests its marker
-  const dim3 check_grid((unsigned)((a.plan.n_items + 64 * W - 1) / (64 * W)));
+  const dim3 check_grid = recheck_grid(a.plan.n_items, n_cu);
   hipLaunchKernelGGL((chunkattn::chunk_attn_recheck<D, T, W>), check_grid, dim3(64 * W), kLds,
                      stream, a);
   return hipGetLastError();
 }
 
 template <int W>
-hipError_t launch_w(const KernelArgs& a, int n_persist, int head_dim, int dtype,
+hipError_t launch_w(const KernelArgs& a, int n_persist, int n_cu, int head_dim, int dtype,
                     hipStream_t stream) {
   if (head_dim == 128)
-    return dtype == CHUNKATTN_BF16 ? launch_t<128, __bf16, W>(a, n_persist, stream)
-                                   : launch_t<128, float, W>(a, n_persist, stream);
-  return dtype == CHUNKATTN_BF16 ? launch_t<64, __bf16, W>(a, n_persist, stream)
-                                 : launch_t<64, float, W>(a, n_persist, stream);
+    return dtype == CHUNKATTN_BF16 ? launch_t<128, __bf16, W>(a, n_persist, n_cu, stream)
+                                   : launch_t<128, float, W>(a, n_persist, n_cu, stream);
+  return dtype == CHUNKATTN_BF16 ? launch_t<64, __bf16, W>(a, n_persist, n_cu, stream)
+                                 : launch_t<64, float, W>(a, n_persist, n_cu, stream);
 }
 
 // The 384-row main pass (48 rows per wave, persistent like the 256-row one):
@@ -344,8 +350,8 @@ hipError_t launch_w(const KernelArgs& a, int n_persist, int head_dim, int dtype,
 // items of several; then the recheck (three 128-row items per marked block).
 // a: the main pass (work items of one or more 384-row blocks); blocks: the same
 // call planned with one block per item, for the recheck.
-hipError_t launch_wide(const KernelArgs& a, const KernelArgs& blocks, int n_persist, bool exact,
-                       hipStream_t stream) {
+hipError_t launch_wide(const KernelArgs& a, const KernelArgs& blocks, int n_persist, int n_cu,
+                       bool exact, hipStream_t stream) {
   if (!a.queue || n_persist < 1 || a.plan.n_xcd > kQueueWords) return hipErrorInvalidValue;
   hipLaunchKernelGGL(chunkattn::queue_clear, dim3(1), dim3(64), 0, stream, a.queue,
                      a.plan.n_xcd);
@@ -359,17 +365,16 @@ hipError_t launch_wide(const KernelArgs& a, const KernelArgs& blocks, int n_pers
                      chunkattn::kPingPongLdsBytes<128>, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chunkattn::chunk_attn_recheck_wide<4>,
-                     dim3((unsigned)((blocks.plan.n_items + 255) / 256)), dim3(256),
-                     chunkattn::kSyncLdsBytes<128>, stream, blocks);
+  hipLaunchKernelGGL(chunkattn::chunk_attn_recheck_wide<4>, recheck_grid(blocks.plan.n_items, n_cu),
+                     dim3(256), chunkattn::kSyncLdsBytes<128>, stream, blocks);
   return hipGetLastError();
 }
 
 hipError_t launch(const KernelArgs& a, const KernelArgs& blocks, int block_rows, int n_persist,
-                  int head_dim, int dtype, bool exact, hipStream_t stream) {
-  if (block_rows == 384) return launch_wide(a, blocks, n_persist, exact, stream);
-  return block_rows == 128 ? launch_w<4>(a, n_persist, head_dim, dtype, stream)
-                           : launch_w<8>(a, n_persist, head_dim, dtype, stream);
+                  int n_cu, int head_dim, int dtype, bool exact, hipStream_t stream) {
+  if (block_rows == 384) return launch_wide(a, blocks, n_persist, n_cu, exact, stream);
+  return block_rows == 128 ? launch_w<4>(a, n_persist, n_cu, head_dim, dtype, stream)
+                           : launch_w<8>(a, n_persist, n_cu, head_dim, dtype, stream);
 }
 
 hipError_t allow_wide_lds() {
@@ -459,7 +464,7 @@ int run(chunkattn_ctx* ctx, const KernelArgs& args, int head_dim, int dtype, voi
   }
   const int n_persist = (int)(main.plan.n_items < ctx->n_cu ? main.plan.n_items : ctx->n_cu);
   const hipError_t e =
-      launch(main, a, bm, n_persist, head_dim, dtype, ctx->exact_scale,
+      launch(main, a, bm, n_persist, ctx->n_cu, head_dim, dtype, ctx->exact_scale,
              static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return set_err(&ctx->err, CHUNKATTN_ELAUNCH, "kernel launch failed: %s",

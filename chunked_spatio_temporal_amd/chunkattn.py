@@ -53,6 +53,8 @@ def load_library():
     lib.chunkattn_ctx_call_block_rows.argtypes = [vp, i32, i32]
     lib.chunkattn_ctx_set_item_blocks.restype = i32
     lib.chunkattn_ctx_set_item_blocks.argtypes = [vp, i32]
+    lib.chunkattn_ctx_set_tail_split.restype = i32
+    lib.chunkattn_ctx_set_tail_split.argtypes = [vp, i32, i32]
     lib.chunkattn_create.restype = i32
     lib.chunkattn_create.argtypes = [ctypes.POINTER(vp), i32, ctypes.c_uint]
     lib.chunkattn_destroy.restype = i32
@@ -167,6 +169,12 @@ class Context:
         """Query rows per work item of a call with this head_dim and dtype code."""
         return int(load_library().chunkattn_ctx_call_block_rows(self.handle, int(head_dim),
                                                                 int(dtype)))
+
+    def set_tail_split(self, items: int, parts: int = 0) -> None:
+        """Key-axis split of the last `items` work items into `parts` (-1: chosen
+        per call, 0: never)."""
+        _check(load_library().chunkattn_ctx_set_tail_split(self.handle, int(items), int(parts)),
+               self.handle)
 
     def set_item_blocks(self, blocks: int) -> None:
         """384-row query blocks per work item (0: chosen per call, 1..8: fixed)."""

@@ -91,6 +91,11 @@ struct KernelArgs {
   // n_xcd counts the claims on die x's share (claim_word_item); queue_clear
   // zeroes the words on the same stream just before the launch.
   unsigned long long* queue;
+  // Key-axis split (plan.split_parts > 1, 384-row items only): per split item
+  // and part, a slot of kSplitSlotFloats floats for the partial O and l, and
+  // per split item an arrival counter, zero at launch.
+  float* split_ws;
+  unsigned* split_cnt;
 
   // Physical entry of batch index b (b > -ring_slots).
   __host__ __device__ __forceinline__ int64_t entry(int b) const {
@@ -667,6 +672,14 @@ __global__ __launch_bounds__(W * 64, 8 / W) void chunk_attn_recheck(KernelArgs a
 // launch has to leave them clean.
 __global__ void queue_clear(unsigned long long* words, int n) {
   if ((int)threadIdx.x < n) words[threadIdx.x] = 0ull;
+}
+
+// Zeroes n 32-bit words (grid-stride): the arrival counters of a key-split
+// launch, cleared on its stream just before the main pass.
+__global__ void words_clear(unsigned* words, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    words[i] = 0u;
 }
 
 // Writes the decoded work item of every workgroup slot (7 ints each), using

@@ -45,6 +45,11 @@ namespace chunkattn {
 constexpr int kWideRows = 48;            // query rows per wave
 constexpr int kWideWaves = 8;
 constexpr int kWideBlockRows = kWideRows * kWideWaves;  // 384 rows per work item
+// Workspace slot of one part of a key-split item: the partial O of 8 waves x
+// 3 query blocks x 8 dim blocks x 64 lanes x 4 floats, in register order, then
+// the partial l of 8 waves x 3 query blocks x 64 lanes.
+constexpr int kSplitOFloats = kWideWaves * 3 * 8 * 64 * 4;
+constexpr int kSplitSlotFloats = kSplitOFloats + kWideWaves * 3 * 64;
 
 __device__ __forceinline__ int wide_kswz(int r) { return r & 15; }        // 16-byte blocks
 __device__ __forceinline__ int wide_vswz(int r) { return 2 * (r & 7); }   // 16-byte blocks
@@ -73,6 +78,41 @@ __device__ __forceinline__ void load_lds16x2_split(const void* sbase0, const voi
       : "v"(voff), "s"(sb0), "s"(sb1), "s"(m0)
       : "memory");
 #endif
+}
+
+// Device-scope (sc1) store and loads of key-split partials: written through to
+// the memory every die sees and read from it, so neither side needs a fence
+// that writes back or invalidates a whole L2 (other CUs keep their K/V tiles
+// cached).  The loads wait for their data inside the same asm block.
+__device__ __forceinline__ void store_device16(float* p, const f32x4_t& x) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(x) : "memory");
+}
+__device__ __forceinline__ void store_device4(float* p, float x) {
+  asm volatile("global_store_dword %0, %1, off sc1" : : "v"(p), "v"(x) : "memory");
+}
+// eight 16-byte loads at p, p + stride, ... (stride in floats)
+__device__ __forceinline__ void load_device16x8(const float* p, int stride, f32x4_t (&x)[8]) {
+  asm volatile(
+      "global_load_dwordx4 %0, %8, off sc1\n\t"
+      "global_load_dwordx4 %1, %9, off sc1\n\t"
+      "global_load_dwordx4 %2, %10, off sc1\n\t"
+      "global_load_dwordx4 %3, %11, off sc1\n\t"
+      "global_load_dwordx4 %4, %12, off sc1\n\t"
+      "global_load_dwordx4 %5, %13, off sc1\n\t"
+      "global_load_dwordx4 %6, %14, off sc1\n\t"
+      "global_load_dwordx4 %7, %15, off sc1\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+        "=&v"(x[6]), "=&v"(x[7])
+      : "v"(p), "v"(p + stride), "v"(p + 2 * stride), "v"(p + 3 * stride),
+        "v"(p + 4 * stride), "v"(p + 5 * stride), "v"(p + 6 * stride), "v"(p + 7 * stride)
+      : "memory");
+}
+__device__ __forceinline__ float load_device4(const float* p) {
+  float x;
+  asm volatile("global_load_dword %0, %1, off sc1\n\ts_waitcnt vmcnt(0)" : "=&v"(x) : "v"(p)
+               : "memory");
+  return x;
 }
 
 __device__ __forceinline__ void pin(f32x4_t& x) { asm volatile("" : "+v"(x)); }
@@ -138,7 +178,11 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
   const int n_tiles = (total + kBN - 1) / kBN;  // key/value tiles per block
   static_assert(!kStream || kQB == 3, "multi-block items run with three query blocks per wave");
   const int nblk = kStream ? (it.q_rows + kWideBlockRows - 1) / kWideBlockRows : 1;
-  const int n_stream = nblk * n_tiles;           // tiles of the whole stream
+  // the walk: key tiles [t0, t0 + nt) (a part of a key-split item walks its
+  // share of the tiles), or nblk times all of them in the stream form
+  const int t0 = kStream ? 0 : it.t_lo;
+  const int nt = kStream ? n_tiles : it.t_hi - it.t_lo;
+  const int n_stream = kStream ? nblk * n_tiles : nt;  // tiles of the whole stream
   const int64_t rs = a.row_stride;
 
   const int64_t e = a.entry(it.b);
@@ -597,9 +641,9 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
 
   // ---- prologue: the first three groups of key/value loads and the Q
   // loads go out together (one memory latency for all), then Q is scaled
-  issue(0, 0);
-  issue(1, tile_ahead(0, 1));
-  issue(2, tile_ahead(0, 2));
+  issue(0, t0);
+  issue(1, tile_ahead(t0, 1));
+  issue(2, tile_ahead(t0, 2));
   load_q(0);
   wait_vmem();
   scale_q();
@@ -609,14 +653,14 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
 
   using F = std::false_type;
   using Tr = std::true_type;
-  if (n_tiles == 1) {
+  if (nt == 1) {
     // one tile per block: every step opens and closes a block
-    step(0, 0, 0, Tr{}, F{}, Tr{});
+    step(0, t0, 0, Tr{}, F{}, Tr{});
     for (int jb = 1; jb < nblk; ++jb) step(jb, 0, jb, F{}, Tr{}, Tr{});
   } else {
-    step(0, 0, 0, Tr{}, F{}, F{});
-    for (int t = 1; t + 1 < n_tiles; ++t) step(t, t, 0, F{}, F{}, F{});
-    step(n_tiles - 1, n_tiles - 1, 0, F{}, F{}, Tr{});
+    step(0, t0, 0, Tr{}, F{}, F{});
+    for (int u = 1; u + 1 < nt; ++u) step(u, t0 + u, 0, F{}, F{}, F{});
+    step(nt - 1, t0 + nt - 1, 0, F{}, F{}, Tr{});
     for (int jb = 1; jb < nblk; ++jb) {
       const int u0 = jb * n_tiles;
       step(u0, 0, jb, F{}, Tr{}, F{});
@@ -631,6 +675,53 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
   // ---- epilogue: the last block
   float l_last[kQB];
   take_l(l_last);
+  if constexpr (!kStream) {
+    if (it.part >= 0) {
+      // A part of a key-split item.  Without a maximum the parts' sums add:
+      // O = (O_1 + ... + O_S) / (l_1 + ... + l_S).  Each part stores its
+      // unnormalised O and l; the part that arrives last adds all of them in
+      // part order and finishes the block.
+      const int parts = a.plan.split_parts;
+      const int l6 = lane_now();
+      auto slot_of = [&](int part) __attribute__((always_inline)) {
+        return a.split_ws + ((size_t)it.split_idx * parts + part) * kSplitSlotFloats;
+      };
+      {
+        float* ws = slot_of(it.part);
+#pragma unroll
+        for (int q3 = 0; q3 < kQB; ++q3) {
+#pragma unroll
+          for (int db = 0; db < kDB; ++db)
+            store_device16(ws + (((wave * 3 + q3) * kDB + db) * 64 + l6) * 4, oacc[q3][db]);
+          store_device4(ws + kSplitOFloats + (wave * 3 + q3) * 64 + l6, l_last[q3]);
+        }
+      }
+      // the partial has reached device scope before this workgroup arrives
+      asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+      wg_barrier();
+      if (tid == 0)
+        range_flags[2] = atomicAdd(&a.split_cnt[it.split_idx], 1u) == (unsigned)(parts - 1);
+      wg_barrier();
+      if (range_flags[2] == 0) return;
+      // all parts, the own one read back too, added in part order: the sum
+      // does not depend on which part arrived last
+      for (int p = 0; p < parts; ++p) {
+        const float* ws = slot_of(p);
+#pragma unroll
+        for (int q3 = 0; q3 < kQB; ++q3) {
+          f32x4_t x[kDB];
+          load_device16x8(ws + ((wave * 3 + q3) * kDB * 64 + l6) * 4, 64 * 4, x);
+#pragma unroll
+          for (int db = 0; db < kDB; ++db)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              oacc[q3][db][e] = p == 0 ? x[db][e] : oacc[q3][db][e] + x[db][e];
+          const float lp = load_device4(ws + kSplitOFloats + (wave * 3 + q3) * 64 + l6);
+          l_last[q3] = p == 0 ? lp : l_last[q3] + lp;
+        }
+      }
+    }
+  }
   finish_block(nblk - 1, l_last);
 }
 
@@ -644,7 +735,9 @@ template <bool kStream, bool kExact>
 __device__ __forceinline__ void wide_persistent(const KernelArgs& a, unsigned char* smem) {
   __shared__ long long next_item;  // >= 0 item, -1 none left, -2 claim again
   __shared__ int used_up;          // thread 0: dies (from our own on) found empty
-  __shared__ int range_flags[2];   // some row of a block (by block parity) left fp32's range
+  // [0], [1]: some row of a block (by block parity) left fp32's range; [2]:
+  // this workgroup finishes a key-split item
+  __shared__ int range_flags[3];
   const int nx = a.plan.n_xcd;
   const int die = (int)(__builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) % (unsigned)nx);
   auto die_at = [&](int k) __attribute__((always_inline)) {
@@ -655,7 +748,9 @@ __device__ __forceinline__ void wide_persistent(const KernelArgs& a, unsigned ch
     long long w = -1;
     for (; k < nx; ++k) {
       const unsigned long long old = atomicAdd(&a.queue[die_at(k)], 1ull);
-      w = claim_word_item(a.plan, die_at(k), old);
+      // (items of several blocks are never split)
+      w = kStream ? claim_word_item(a.plan, die_at(k), old)
+                  : claim_word_unit(a.plan, die_at(k), old);
       if (w >= 0) break;
     }
     used_up = k;
@@ -685,13 +780,14 @@ __device__ __forceinline__ void wide_persistent(const KernelArgs& a, unsigned ch
       if (threadIdx.x == 0) {
         long long nw = -1;
         if (k < nx) {
-          nw = claim_word_item(a.plan, die_at(k), ticket);
+          nw = kStream ? claim_word_item(a.plan, die_at(k), ticket)
+                       : claim_word_unit(a.plan, die_at(k), ticket);
           if (nw < 0) nw = -2;
         }
         next_item = nw;
       }
     };
-    const Item it = decode(a.plan, w);
+    const Item it = kStream ? decode(a.plan, w) : decode_unit(a.plan, w);
     if (kStream || it.q_rows > 2 * 16 * kWideWaves)
       attn_item_wide<3, kStream, kExact>(a, it, smem, range_flags, after_prologue);
     else if (it.q_rows > 16 * kWideWaves)

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -52,6 +53,13 @@ struct chunkattn_ctx {
   int item_blocks = 0;
   // scores scaled in fp32 (CHUNKATTN_FLAG_EXACT_SCALE)
   bool exact_scale = false;
+  // key-axis split of the last items: items -1 = chosen per call, 0 = off,
+  // > 0 = that many items into `split_parts` parts
+  int split_items = -1;
+  int split_parts = 0;
+  // stream-ordered pool of the split workspaces (created on first use)
+  hipMemPool_t split_pool = nullptr;
+  std::mutex split_pool_mu;
   // device, (kQueueSlots + kCaptureSlots) * kQueueWords words
   unsigned long long* queue = nullptr;
   // device address of this device's `scratch` array (noalloc entry point)
@@ -83,6 +91,45 @@ int call_block_rows(const chunkattn_ctx* ctx, int head_dim, int dtype) {
 }
 
 thread_local std::string g_thread_err;
+
+constexpr int kMaxSplitParts = 8;
+
+// Key-axis split of the last items of a launch with one 384-row block per
+// item: {items, parts}, {0, 0} for none.  When a launch has few items per CU
+// (fewer than 8), the last wave of items decides when it ends: the last items
+// in work order are cut into 4 parts each, so the end of the launch is made of
+// quarter items.  How many: n_cu below 3 items per CU, 1.5 n_cu from 3 to 7
+// (measured best of n_cu/2..2.7 n_cu and 2, 4 and 8 parts on the 5-head and
+// 12-head 480p queues; 2 parts gained about half as much).  Every part walks
+// at least one key tile.
+struct SplitChoice {
+  int64_t items;
+  int parts;
+};
+SplitChoice split_choice(const chunkattn_ctx* ctx, const Plan& p) {
+  if (ctx->split_items == 0 || p.n_items == 0) return {0, 0};
+  int min_keys = 0x7fffffff;
+  for (int b = 0; b < p.n_batch; ++b) {
+    const int keys =
+        (b >= p.first_pred ? p.lpred : 0) + (b == p.n_batch - 1 ? p.lown_last : p.lown);
+    min_keys = keys < min_keys ? keys : min_keys;
+  }
+  const int min_tiles = (min_keys + chunkattn::kBN - 1) / chunkattn::kBN;
+  int64_t items;
+  int parts;
+  if (ctx->split_items > 0) {
+    items = ctx->split_items;
+    parts = ctx->split_parts;
+  } else {
+    const int64_t per_cu = p.n_items / (ctx->n_cu > 0 ? ctx->n_cu : 1);
+    if (per_cu >= 8) return {0, 0};
+    items = per_cu < 3 ? ctx->n_cu : ctx->n_cu * 3 / 2;
+    parts = 4;
+  }
+  if (parts > min_tiles) parts = min_tiles;
+  if (parts < 2) return {0, 0};
+  return {items < p.n_items ? items : p.n_items, parts};
+}
 
 constexpr int kMaxItemBlocks = 8;
 
@@ -357,6 +404,13 @@ hipError_t launch_wide(const KernelArgs& a, const KernelArgs& blocks, int n_pers
                      a.plan.n_xcd);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.plan.split_parts > 1) {
+    const int64_t n = a.plan.n_items - a.plan.split_from;
+    hipLaunchKernelGGL(chunkattn::words_clear, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, a.split_cnt, n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const bool multi = a.plan.bm > chunkattn::kWideBlockRows;
   auto kernel = multi ? (exact ? chunkattn::chunk_attn_fwd_wide_stream_exact
                                : chunkattn::chunk_attn_fwd_wide_stream)
@@ -410,6 +464,29 @@ struct DeviceGuard {
   }
 };
 
+// The context's pool for split workspaces: device memory, kept by the pool
+// between calls (no release threshold), created on first use.
+hipError_t split_pool(chunkattn_ctx* ctx) {
+  std::lock_guard<std::mutex> lock(ctx->split_pool_mu);
+  if (ctx->split_pool) return hipSuccess;
+  hipMemPoolProps props = {};
+  props.allocType = hipMemAllocationTypePinned;
+  props.handleTypes = hipMemHandleTypeNone;
+  props.location.type = hipMemLocationTypeDevice;
+  props.location.id = ctx->device;
+  hipMemPool_t pool = nullptr;
+  hipError_t e = hipMemPoolCreate(&pool, &props);
+  if (e != hipSuccess) return e;
+  uint64_t keep = ~0ull;
+  e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+  if (e != hipSuccess) {
+    (void)hipMemPoolDestroy(pool);
+    return e;
+  }
+  ctx->split_pool = pool;
+  return hipSuccess;
+}
+
 // Launches the main pass (and the recheck) of a prepared argument block.
 // fixed_queue: NULL = the work-queue slot comes from the context's buffer;
 // otherwise the persistent pass uses these kStaticScratchWords words (the
@@ -432,14 +509,17 @@ int run(chunkattn_ctx* ctx, const KernelArgs& args, int head_dim, int dtype, voi
                      "device has %d dies; the static work queue holds %d claim words",
                      a.plan.n_xcd, kStaticScratchWords);
     a.queue = fixed_queue;
-  } else if (bm >= 256) {
+  }
+  bool capturing = false;
+  if (bm >= 256 && !fixed_queue) {
     // one claim word per die must fit in a slot
     if (a.plan.n_xcd > kQueueWords) a.plan.n_xcd = 1;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap) != hipSuccess)
       return set_err(&ctx->err, CHUNKATTN_ELAUNCH, "cannot query the stream's capture state");
+    capturing = cap == hipStreamCaptureStatusActive;
     unsigned slot;
-    if (cap == hipStreamCaptureStatusActive) {
+    if (capturing) {
       const unsigned c = ctx->next_capture.fetch_add(1, std::memory_order_relaxed);
       if (c >= (unsigned)kCaptureSlots) {
         ctx->next_capture.store(kCaptureSlots, std::memory_order_relaxed);
@@ -462,10 +542,34 @@ int run(chunkattn_ctx* ctx, const KernelArgs& args, int head_dim, int dtype, voi
                                        nb * bm, p.n_xcd, p.lq_last, p.lown_last);
     }
   }
-  const int n_persist = (int)(main.plan.n_items < ctx->n_cu ? main.plan.n_items : ctx->n_cu);
+  // One block per item, few items per CU: cut the last items along the keys.
+  // The workspace comes from the context's stream-ordered pool and returns to
+  // it after the launch, so calls on other streams get their own.  Not under
+  // graph capture and not for the no-allocation entry point.
+  void* ws = nullptr;
+  if (bm == 384 && main.plan.bm == 384 && !fixed_queue && !capturing) {
+    const SplitChoice sc = split_choice(ctx, a.plan);
+    if (sc.items > 0) {
+      const size_t ws_bytes =
+          (size_t)sc.items * sc.parts * chunkattn::kSplitSlotFloats * sizeof(float);
+      const size_t cnt_bytes = ((size_t)sc.items * sizeof(unsigned) + 255) & ~(size_t)255;
+      if (split_pool(ctx) == hipSuccess &&
+          hipMallocFromPoolAsync(&ws, ws_bytes + cnt_bytes, ctx->split_pool,
+                                 static_cast<hipStream_t>(stream)) == hipSuccess) {
+        main.plan = chunkattn::plan_with_split(main.plan, sc.items, sc.parts);
+        main.split_ws = static_cast<float*>(ws);
+        main.split_cnt = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + ws_bytes);
+      } else {
+        ws = nullptr;  // no workspace: run unsplit
+        (void)hipGetLastError();
+      }
+    }
+  }
+  const int n_persist = (int)(main.plan.n_units < ctx->n_cu ? main.plan.n_units : ctx->n_cu);
   const hipError_t e =
       launch(main, a, bm, n_persist, ctx->n_cu, head_dim, dtype, ctx->exact_scale,
              static_cast<hipStream_t>(stream));
+  if (ws) (void)hipFreeAsync(ws, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return set_err(&ctx->err, CHUNKATTN_ELAUNCH, "kernel launch failed: %s",
                    hipGetErrorString(e));
@@ -492,6 +596,18 @@ int chunkattn_ctx_block_rows(const chunkattn_ctx* ctx) {
 
 int chunkattn_ctx_call_block_rows(const chunkattn_ctx* ctx, int head_dim, int dtype) {
   return ctx ? call_block_rows(ctx, head_dim, dtype) : 0;
+}
+
+int chunkattn_ctx_set_tail_split(chunkattn_ctx* ctx, int items, int parts) {
+  if (!ctx) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "ctx must be non-NULL");
+  if (items < -1 || (items > 0 && (parts < 2 || parts > kMaxSplitParts)))
+    return set_err(&ctx->err, CHUNKATTN_EINVAL,
+                   "tail split: items %d (-1, 0 or > 0), parts %d (2..%d)", items, parts,
+                   kMaxSplitParts);
+  ctx->split_items = items;
+  ctx->split_parts = items > 0 ? parts : 0;
+  ctx->err.clear();
+  return CHUNKATTN_OK;
 }
 
 int chunkattn_ctx_set_item_blocks(chunkattn_ctx* ctx, int blocks) {
@@ -589,9 +705,11 @@ int chunkattn_create(chunkattn_ctx** out, int device_ordinal, unsigned flags) {
 }
 
 int chunkattn_destroy(chunkattn_ctx* ctx) {
-  if (ctx && ctx->queue) {
+  if (ctx && (ctx->queue || ctx->split_pool)) {
     DeviceGuard g(ctx->device);
-    (void)hipFree(ctx->queue);
+    if (ctx->queue) (void)hipFree(ctx->queue);
+    // released once the last stream-ordered free has run
+    if (ctx->split_pool) (void)hipMemPoolDestroy(ctx->split_pool);
   }
   delete ctx;
   return CHUNKATTN_OK;

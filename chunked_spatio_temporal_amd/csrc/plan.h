@@ -51,10 +51,19 @@ struct Plan {
   int n_xcd;       // dies for the launch-order renumbering (>= 1)
   int64_t n_items;
   int64_t n_items_pred;  // items of entries with a predecessor (scheduled first)
+  // Key-axis split of the last items (split_parts = 1: none).  Items
+  // [split_from, n_items) of the work order are each cut into split_parts
+  // units along their key tiles; the launch runs n_units units.
+  int64_t split_from;
+  int split_parts;
+  int64_t n_units;
 };
 
 struct Item {
   int b, h, q0, q_rows, pred_rows, own_rows;
+  // key tiles [t_lo, t_hi) of the item's walk; part >= 0 for a unit of a
+  // split item (split_idx: its index among the split items), -1 otherwise
+  int t_lo, t_hi, part, split_idx;
 };
 
 CA_HD Plan make_plan(int n_batch, int first_pred, int heads, int lq, int lown, int lpred,
@@ -77,6 +86,20 @@ CA_HD Plan make_plan(int n_batch, int first_pred, int heads, int lq, int lown, i
   p.n_items = n_batch > 0 ? (int64_t)(n_batch - 1) * per_entry + per_last : 0;
   const int n_pred = n_batch - p.first_pred;  // the last entry is among them if n_pred > 0
   p.n_items_pred = n_pred > 0 ? (int64_t)(n_pred - 1) * per_entry + per_last : 0;
+  p.split_from = p.n_items;
+  p.split_parts = 1;
+  p.n_units = p.n_items;
+  return p;
+}
+
+// The same plan with its last n_split items (work order) cut into `parts`
+// units each along the key axis.
+CA_HD Plan plan_with_split(Plan p, int64_t n_split, int parts) {
+  if (n_split > p.n_items) n_split = p.n_items;
+  if (parts < 2 || n_split <= 0) return p;
+  p.split_from = p.n_items - n_split;
+  p.split_parts = parts;
+  p.n_units = p.split_from + n_split * parts;
   return p;
 }
 // Every entry the same size.
@@ -164,7 +187,47 @@ CA_HD Item decode(const Plan& p, int64_t w) {
   it.q_rows = left < p.bm ? left : p.bm;
   it.pred_rows = b >= p.first_pred ? p.lpred : 0;
   it.own_rows = lown;
+  it.t_lo = 0;
+  it.t_hi = (it.pred_rows + it.own_rows + 63) / 64;
+  it.part = -1;
+  it.split_idx = -1;
   return it;
+}
+
+// Work unit u of a plan with a key-axis split: units [0, split_from) are the
+// items themselves; unit split_from + s is part s % split_parts of item
+// split_from + s / split_parts, whose key tiles [T*part/parts, T*(part+1)/parts)
+// it walks (T: the item's tiles).
+CA_HD Item decode_unit(const Plan& p, int64_t u) {
+  if (u < p.split_from) return decode(p, u);
+  const int64_t s = u - p.split_from;
+  Item it = decode(p, p.split_from + s / p.split_parts);
+  const int part = (int)(s % p.split_parts);
+  const int t = it.t_hi;
+  it.t_lo = (int)((int64_t)t * part / p.split_parts);
+  it.t_hi = (int)((int64_t)t * (part + 1) / p.split_parts);
+  it.part = part;
+  it.split_idx = (int)(s / p.split_parts);
+  return it;
+}
+
+// Persistent claim over units.  Without a split it is claim_word_item.  With
+// one, die x's queue holds its even share of the unsplit long items, then of
+// the unsplit short items, then of the split units (each a contiguous range),
+// so the small units come last on every die.
+CA_HD int64_t claim_word_unit(const Plan& p, int x, unsigned long long old) {
+  if (p.split_parts <= 1) return claim_word_item(p, x, old);
+  const int64_t a = p.n_items_pred < p.split_from ? p.n_items_pred : p.split_from;
+  const int64_t sizes[3] = {a, p.split_from - a, p.n_units - p.split_from};
+  const int64_t starts[3] = {0, a, p.split_from};
+  int64_t pos = (int64_t)old;
+  for (int k = 0; k < 3; ++k) {
+    const int64_t s0 = die_share_start(sizes[k], x, p.n_xcd);
+    const int64_t cnt = die_share_start(sizes[k], x + 1, p.n_xcd) - s0;
+    if (pos < cnt) return starts[k] + s0 + pos;
+    pos -= cnt;
+  }
+  return -1;
 }
 
 }  // namespace chunkattn

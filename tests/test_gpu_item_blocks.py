@@ -48,10 +48,13 @@ _CTX = {}
 
 
 def ctx_blocks(g):
-    """A context of the default (384-row) item size with g blocks per item."""
+    """A context of the default (384-row) item size with g blocks per item and
+    no key-axis split (items of several blocks are never split, so the
+    one-block reference must not be either for the bitwise comparisons)."""
     if g not in _CTX:
         c = ca.Context(0, 0)
         c.set_item_blocks(g)
+        c.set_tail_split(0)
         _CTX[g] = c
     return _CTX[g]
 

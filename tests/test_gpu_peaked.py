@@ -169,6 +169,7 @@ def test_exact_scale_cross_attention_item_blocks(G):
     for g in (1, G):
         c = ca.Context(0, ca.FLAG_EXACT_SCALE)
         c.set_item_blocks(g)
+        c.set_tail_split(0)
         o = torch.full_like(q, SENTINEL)
         ca.full(q, kt, vt, out=o, ctx=c)
         torch.cuda.synchronize()

@@ -234,6 +234,36 @@ __device__ __forceinline__ void load_lds16_async(const void* sbase, uint32_t vof
 // would drop the other half.)
 __device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32); }
 
+// Lane exchanges on the vector ALU.  v_permlane16_swap trades the odd 16-lane
+// rows of its first operand with the even rows of its second (in each pair of
+// rows); v_permlane32_swap the upper half of the first with the lower half of
+// the second.  Unlike a ds_bpermute they do not go through the LDS pipe, whose
+// queue the other waves' LDS traffic keeps long.  Written as asm with both
+// operands read and written (the compiler used here returns the first result
+// of the corresponding builtin in place of the second); the nops cover the
+// wait states after a VALU write of an operand and before a VALU read of a
+// result.
+__device__ __forceinline__ void swap_rows16(uint32_t& a, uint32_t& b) {
+  asm("s_nop 4\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 2" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap_halves32(uint32_t& a, uint32_t& b) {
+  asm("s_nop 4\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 2" : "+v"(a), "+v"(b));
+}
+
+// x + (x of lane l ^ 16) and x + (x of lane l ^ 32): after a swap of x with a
+// copy of itself each lane holds its own x and its partner's, in an order that
+// does not change an fp32 sum.
+__device__ __forceinline__ float sum_xor16(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap_rows16(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  swap_halves32(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
 // s_waitcnt vmcnt(0): every global load of this wave (including the ones that
 // write LDS directly) has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

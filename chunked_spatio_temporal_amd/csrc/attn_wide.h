@@ -518,9 +518,7 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
       float x = lsum[q3][0];
 #pragma unroll
       for (int c = 1; c < kLs; ++c) x += lsum[q3][c];
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      l_tot[q3] = x;
+      l_tot[q3] = sum_xor32(sum_xor16(x));
 #pragma unroll
       for (int c = 0; c < kLs; ++c) lsum[q3][c] = 0.f;
     }
@@ -548,7 +546,11 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
     // consecutive dims (16 bytes) per pair of db: even g the dims 32m + 4g ..
     // +7 (its own db = 2m values and its partner's), odd g the dims
     // 32m + 16 + 4(g-1) .. +7 (its partner's db = 2m+1 values and its own):
-    // half as many store instructions as 8-byte stores.
+    // half as many store instructions as 8-byte stores.  The trade is one
+    // 16-lane row swap per word pair (x from db 2m, y from db 2m+1): x of the
+    // odd row (g odd) goes to the even row's y, which leaves even g with
+    // {own x, partner's x} and odd g with {partner's y, own y}, each in dim
+    // order.
     const bool odd = (l >> 4) & 1;
     const int col = 8 * (l >> 5) + (odd ? 16 : 0);
 #pragma unroll
@@ -564,9 +566,10 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
         const uint32_t a1 = pack_bf16(oa[2] * inv, oa[3] * inv);
         const uint32_t b0 = pack_bf16(ob2[0] * inv, ob2[1] * inv);
         const uint32_t b1 = pack_bf16(ob2[2] * inv, ob2[3] * inv);
-        const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? a0 : b0), 16);
-        const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? a1 : b1), 16);
-        const u32x4_t v4 = odd ? u32x4_t{r0, r1, b0, b1} : u32x4_t{a0, a1, r0, r1};
+        uint32_t x0 = a0, y0 = b0, x1 = a1, y1 = b1;
+        swap_rows16(x0, y0);
+        swap_rows16(x1, y1);
+        const u32x4_t v4 = {x0, x1, y0, y1};
         if (r < it.q_rows) *reinterpret_cast<u32x4_t*>(orow + 32 * m) = v4;
       }
     }

@@ -21,12 +21,13 @@
 
 // Work-queue slots of a context.  A slot is kQueueWords 64-bit words (one
 // claim word per die), cleared by a kernel on the call's stream right before
-// the persistent (256-row) main pass that uses it.  Eager calls take the next
-// of kQueueSlots slots in turn, so up to kQueueSlots of them may be in flight
-// on different streams at once.  A call made while its stream is being
-// captured into a graph takes a slot of its own from the next kCaptureSlots,
-// never used again by another call of the context: the graph keeps that slot
-// for all its replays, and eager calls or other graphs cannot land on it.
+// the persistent main pass (256- or 384-row items) that uses it.  Eager calls
+// take the next of kQueueSlots slots in turn, so up to kQueueSlots of them may
+// be in flight on different streams at once.  A call made while its stream is
+// being captured into a graph takes a slot of its own from the next
+// kCaptureSlots, never used again by another call of the context: the graph
+// keeps that slot for all its replays, and eager calls or other graphs cannot
+// land on it.
 constexpr int kQueueSlots = 64;
 constexpr int kCaptureSlots = 448;
 constexpr int kQueueWords = 16;

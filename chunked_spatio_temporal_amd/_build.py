@@ -9,6 +9,12 @@ calls build().  Every build recompiles from source, in three steps:
 2. the host code alone, with that device binary embedded and registered at
    load time (``-fcuda-include-gpubinary``, as the HIP driver does itself);
 3. the shared library from the host object and the HIP runtime.
+
+Next to it the same host code is built once more with AddressSanitizer and
+UndefinedBehaviorSanitizer (host pass only, on the same device binary) into
+lib/libchunkattn_hostsan.so, for the CPU tests of the host library under the
+sanitizers (tests/test_host_sanitized.py).  Its sanitizer runtime is not
+linked in: a process loads it with the compiler's ASan runtime preloaded.
 """
 import os
 import subprocess
@@ -19,6 +25,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libchunkattn.so")
+SANITIZED_LIB = os.path.join(LIBDIR, "libchunkattn_hostsan.so")
 SOURCE = os.path.join(CSRC, "chunkattn_api.hip")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 CLANG = os.environ.get("HIP_CLANG", os.path.join(ROCM, "lib", "llvm", "bin", "clang++"))
@@ -30,6 +37,8 @@ DEVICE_ONLY = ["--cuda-device-only",
                # keep the compiler from forming packed fp32 VALU ops
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 HOST_ONLY = ["--cuda-host-only", "-fPIC"]
+# host-side sanitizers (each flag for the host compilation only)
+HOST_SANITIZE = ["-O1", "-g", "-fno-omit-frame-pointer", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]
 
 
 def _run(cmd, verbose):
@@ -38,23 +47,34 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compiles the library; `extra` flags go to both the device and host steps."""
-    os.makedirs(LIBDIR, exist_ok=True)
-    fatbin = LIB + ".hipfb.tmp"
-    obj = LIB + ".o.tmp"
-    tmp = LIB + ".tmp"
+def _host_library(fatbin, out, flags, verbose):
+    obj = out + ".o.tmp"
+    tmp = out + ".tmp"
     try:
-        _run([CLANG, *COMMON, *DEVICE_ONLY, *extra, SOURCE, "-o", fatbin], verbose)
-        _run([CLANG, *COMMON, *HOST_ONLY, *extra, "-Xclang", "-fcuda-include-gpubinary",
+        _run([CLANG, *COMMON, *HOST_ONLY, *flags, "-Xclang", "-fcuda-include-gpubinary",
               "-Xclang", fatbin, "-c", SOURCE, "-o", obj], verbose)
         _run([CLANG, "-shared", obj, "-o", tmp, "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
               f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"], verbose)
-        os.replace(tmp, LIB)
+        os.replace(tmp, out)
     finally:
-        for p in (fatbin, obj, tmp):
+        for p in (obj, tmp):
             if os.path.exists(p):
                 os.remove(p)
+
+
+def build(verbose: bool = False, extra=(), sanitized: bool = True) -> str:
+    """Compiles the library (and, with `sanitized`, its host-sanitized twin);
+    `extra` flags go to both the device and host steps."""
+    os.makedirs(LIBDIR, exist_ok=True)
+    fatbin = LIB + ".hipfb.tmp"
+    try:
+        _run([CLANG, *COMMON, *DEVICE_ONLY, *extra, SOURCE, "-o", fatbin], verbose)
+        _host_library(fatbin, LIB, list(extra), verbose)
+        if sanitized:
+            _host_library(fatbin, SANITIZED_LIB, [*extra, *HOST_SANITIZE], verbose)
+    finally:
+        if os.path.exists(fatbin):
+            os.remove(fatbin)
     return LIB
 
 

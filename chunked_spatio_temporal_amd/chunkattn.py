@@ -14,7 +14,9 @@ import re
 import numpy as np
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "lib", "libchunkattn.so")
+# CHUNKATTN_LIBRARY names another build of the same library (the host-sanitized
+# one of the CPU tests); by default the in-tree build.
+LIB_PATH = os.environ.get("CHUNKATTN_LIBRARY") or os.path.join(PKG, "lib", "libchunkattn.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "chunkattn.h")
 
 OK, EINVAL, EUNSUPPORTED, EDEVICE, ENOMEM, ELAUNCH = range(6)

@@ -704,14 +704,6 @@ __global__ void queue_clear(unsigned long long* words, int n) {
   if ((int)threadIdx.x < n) words[threadIdx.x] = 0ull;
 }
 
-// Zeroes n 32-bit words (grid-stride): the arrival counters of a key-split
-// launch, cleared on its stream just before the main pass.
-__global__ void words_clear(unsigned* words, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    words[i] = 0u;
-}
-
 // Writes the decoded work item of every workgroup slot (7 ints each), using
 // the same plan_slot_work/decode as the attention kernel.
 __global__ void plan_dump(Plan p, int* out, int64_t cap) {

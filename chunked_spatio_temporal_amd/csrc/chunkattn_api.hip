@@ -322,6 +322,17 @@ template __global__ void chunk_attn_recheck<128, __bf16, 8>(KernelArgs);
 template __global__ void chunk_attn_recheck<128, float, 8>(KernelArgs);
 template __global__ void chunk_attn_recheck<64, __bf16, 8>(KernelArgs);
 template __global__ void chunk_attn_recheck<64, float, 8>(KernelArgs);
+
+// The clears before a key-split launch in one kernel: the nq claim words of
+// the work-queue slot and the ncnt arrival counters of the split items (one
+// launch rather than two; a short launch pays a few microseconds per extra
+// kernel).
+__global__ void split_launch_clear(unsigned long long* queue, int nq, unsigned* cnt,
+                                   int64_t ncnt) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nq) queue[i] = 0ull;
+  for (int64_t j = i; j < ncnt; j += (int64_t)gridDim.x * blockDim.x) cnt[j] = 0u;
+}
 }  // namespace chunkattn
 
 namespace {
@@ -401,17 +412,16 @@ hipError_t launch_w(const KernelArgs& a, int n_persist, int n_cu, int head_dim, 
 hipError_t launch_wide(const KernelArgs& a, const KernelArgs& blocks, int n_persist, int n_cu,
                        bool exact, hipStream_t stream) {
   if (!a.queue || n_persist < 1 || a.plan.n_xcd > kQueueWords) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(chunkattn::queue_clear, dim3(1), dim3(64), 0, stream, a.queue,
-                     a.plan.n_xcd);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   if (a.plan.split_parts > 1) {
     const int64_t n = a.plan.n_items - a.plan.split_from;
-    hipLaunchKernelGGL(chunkattn::words_clear, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                       stream, a.split_cnt, n);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(chunkattn::split_launch_clear, dim3((unsigned)((n + 255) / 256)),
+                       dim3(256), 0, stream, a.queue, a.plan.n_xcd, a.split_cnt, n);
+  } else {
+    hipLaunchKernelGGL(chunkattn::queue_clear, dim3(1), dim3(64), 0, stream, a.queue,
+                       a.plan.n_xcd);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const bool multi = a.plan.bm > chunkattn::kWideBlockRows;
   auto kernel = multi ? (exact ? chunkattn::chunk_attn_fwd_wide_stream_exact
                                : chunkattn::chunk_attn_fwd_wide_stream)

@@ -69,6 +69,9 @@ def parse():
                     help="context with the exact-scale flag (scores scaled in fp32)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (counter calibration)")
+    ap.add_argument("--linearity", action="store_true",
+                    help="instead of the one-workload line: queue-step time against the number "
+                         "of chunks, and full attention over the same tokens against their count")
     return ap.parse_args()
 
 
@@ -86,6 +89,9 @@ def main():
     from chunked_spatio_temporal_amd import chunkattn as ca
     from chunked_spatio_temporal_amd import configs, synth
 
+    if args.linearity:
+        bench_linearity(args)
+        return
     name = args.workload or configs.BENCH_WORKLOAD
     if name in configs.NOISE_WORKLOADS:
         bench_noise(args, configs.NOISE_WORKLOADS[name])
@@ -293,6 +299,69 @@ def main():
             record["cpu_baseline"] = cpu_baseline(w, q, k, v, cache, args.cpu_seconds)
 
     print(json.dumps(record), flush=True)
+
+
+def bench_linearity(args):
+    """Cost against video length (DualParal write-up, section 二: with a fixed
+    chunk size the per-step cost grows with the number of chunks, not with its
+    square).  The 40-head 480p queue step (chunks of 6240 tokens, head dim 128,
+    bf16) at 1, 2, 4, 8 and 16 chunks, and full bidirectional attention over
+    the same n x 6240 tokens (one sequence, 40 heads) at n = 1, 2, 4, 8.  One
+    JSON line: milliseconds per call (mean of HIP events over --steps calls
+    after --warmup), FLOPs and TFLOP/s per point."""
+    import torch
+
+    from chunked_spatio_temporal_amd import chunkattn as ca
+    from chunked_spatio_temporal_amd import synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    ca.load_library()
+    L, H, D = 6240, 40, 128
+    scale = D ** -0.5
+    stream = torch.cuda.current_stream(dev)
+    steps, warmup = max(args.steps, 1), args.warmup
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+    queue, full = [], []
+    for n in (1, 2, 4, 8, 16):
+        q, k, v = synth.queue_inputs(n, L, H, D, 20 + n, device=dev, k_rho=0.9)
+        cache = synth.build_cache(k, v)
+        out = torch.empty_like(q)
+        ms = timed(lambda: ca.queue_step(q, k, v, cache, out=out, scale=scale))
+        flops = 4.0 * (L * L + (n - 1) * 2 * L * L) * D * H
+        queue.append({"n_chunks": n, "tokens": n * L, "ms": round(ms, 4),
+                      "ms_per_chunk": round(ms / n, 4), "flops": flops,
+                      "tflops": round(flops / ms / 1e9, 1)})
+        print(f"[bench] queue n={n}: {ms:.3f} ms", file=sys.stderr, flush=True)
+        del q, k, v, cache, out
+    for n in (1, 2, 4, 8):
+        S = n * L
+        q = synth.normal((1, S, H, D), 30 + n, synth.Q_ID, dev)
+        k = synth.normal((1, S, H, D), 30 + n, synth.K_ID, dev)
+        v = synth.normal((1, S, H, D), 30 + n, synth.V_ID, dev)
+        out = torch.empty_like(q)
+        ms = timed(lambda: ca.full(q, k, v, out=out, scale=scale))
+        flops = 4.0 * S * S * D * H
+        full.append({"tokens": S, "ms": round(ms, 4), "ms_per_6240_tokens": round(ms / n, 4),
+                     "flops": flops, "tflops": round(flops / ms / 1e9, 1)})
+        print(f"[bench] full S={S}: {ms:.3f} ms", file=sys.stderr, flush=True)
+        del q, k, v, out
+    print(json.dumps({"report": "linearity", "unit": "ms per call", "chunk_len": L, "heads": H,
+                      "head_dim": D, "dtype": "bf16", "steps": steps, "warmup": warmup,
+                      "queue_step": queue, "full_attention_same_tokens": full}), flush=True)
 
 
 def bench_noise(args, w):

@@ -40,6 +40,8 @@ def kernel_hash() -> str:
 
 def kernel_name(block_rows: int, D: int, dtype: str) -> str:
     """The main-pass kernel a call with this work-item size runs."""
+    if block_rows == 64:
+        return f"chunk_attn_fwd_f32<{D}>"
     if block_rows == 384:
         return "chunk_attn_fwd_wide"
     if block_rows == 256:

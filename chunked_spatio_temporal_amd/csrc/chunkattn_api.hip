@@ -12,6 +12,7 @@
 #include <new>
 #include <string>
 
+#include "attn_f32.h"
 #include "attn_kernel.h"
 #include "attn_pingpong.h"
 #include "attn_wide.h"
@@ -76,16 +77,22 @@ namespace {
 using chunkattn::KernelArgs;
 using chunkattn::Plan;
 
-constexpr int kMinBlockRows = 128;  // smallest work item (4 waves); bounds the grid
+constexpr int kMinBlockRows = 128;  // smallest bf16 work item (4 waves); bounds the grid
+
+// Smallest work item of a call of this dtype (fp32 calls: 64 rows).
+int min_block_rows(int dtype) {
+  return dtype == CHUNKATTN_F32 ? chunkattn::kF32BlockRows : kMinBlockRows;
+}
 
 // The 384-row kernel exists for bf16 storage and head_dim 128 only.
 bool wide_supported(int head_dim, int dtype) { return head_dim == 128 && dtype == CHUNKATTN_BF16; }
 
-// Query rows per work item of one call.  Contexts of 128 or 256 rows use that
-// size for every call; the default context (and a 384-row one) uses 384-row
-// items where the 384-row kernel exists (bf16, head_dim 128) and 256-row items
-// for every other call.
+// Query rows per work item of one call.  fp32 calls always run the fp32
+// kernel (64-row items).  For bf16 calls, contexts of 128 or 256 rows use that
+// size; the default context (and a 384-row one) uses 384-row items where the
+// 384-row kernel exists (head_dim 128) and 256-row items otherwise.
 int call_block_rows(const chunkattn_ctx* ctx, int head_dim, int dtype) {
+  if (dtype == CHUNKATTN_F32) return chunkattn::kF32BlockRows;
   if (ctx->block_rows == 128 || ctx->block_rows == 256) return ctx->block_rows;
   // exact-scale contexts: the 256-row pass rounds the scaled Q to bf16
   return wide_supported(head_dim, dtype) ? 384 : ctx->exact_scale ? 128 : 256;
@@ -239,7 +246,8 @@ int validate_queue(std::string* err, const void* q, const void* k, const void* v
     return set_err(err, CHUNKATTN_EINVAL, "out overlaps an input tensor");
   const long double q_rows = window ? 2.0L * L : (long double)L;
   const long double items =
-      (long double)n * heads * ((long long)((q_rows + kMinBlockRows - 1) / kMinBlockRows));
+      (long double)n * heads *
+      ((long long)((q_rows + min_block_rows(dtype) - 1) / min_block_rows(dtype)));
   if (items > 2147483647.0L)
     return set_err(err, CHUNKATTN_EUNSUPPORTED, "too many work items for one launch");
   return CHUNKATTN_OK;
@@ -296,7 +304,7 @@ int validate_full(std::string* err, const void* q, const void* k, const void* v,
   if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kb) || overlaps(out, qb, v, kb))
     return set_err(err, CHUNKATTN_EINVAL, "out overlaps an input tensor");
   const long double items =
-      (long double)batch * heads * ((lq + kMinBlockRows - 1) / kMinBlockRows);
+      (long double)batch * heads * ((lq + min_block_rows(dtype) - 1) / min_block_rows(dtype));
   if (items > 2147483647.0L)
     return set_err(err, CHUNKATTN_EUNSUPPORTED, "too many work items for one launch");
   return CHUNKATTN_OK;
@@ -307,21 +315,15 @@ int validate_full(std::string* err, const void* q, const void* k, const void* v,
 // Every kernel configuration the host can launch, instantiated explicitly.
 namespace chunkattn {
 template __global__ void chunk_attn_fwd_pingpong<128, __bf16>(KernelArgs);
-template __global__ void chunk_attn_fwd_pingpong<128, float>(KernelArgs);
 template __global__ void chunk_attn_fwd_pingpong<64, __bf16>(KernelArgs);
-template __global__ void chunk_attn_fwd_pingpong<64, float>(KernelArgs);
 template __global__ void chunk_attn_fwd<128, __bf16, 4>(KernelArgs);
 template __global__ void chunk_attn_recheck<128, __bf16, 4>(KernelArgs);
-template __global__ void chunk_attn_fwd<128, float, 4>(KernelArgs);
-template __global__ void chunk_attn_recheck<128, float, 4>(KernelArgs);
 template __global__ void chunk_attn_fwd<64, __bf16, 4>(KernelArgs);
 template __global__ void chunk_attn_recheck<64, __bf16, 4>(KernelArgs);
-template __global__ void chunk_attn_fwd<64, float, 4>(KernelArgs);
-template __global__ void chunk_attn_recheck<64, float, 4>(KernelArgs);
 template __global__ void chunk_attn_recheck<128, __bf16, 8>(KernelArgs);
-template __global__ void chunk_attn_recheck<128, float, 8>(KernelArgs);
 template __global__ void chunk_attn_recheck<64, __bf16, 8>(KernelArgs);
-template __global__ void chunk_attn_recheck<64, float, 8>(KernelArgs);
+template __global__ void chunk_attn_fwd_f32<128>(KernelArgs);
+template __global__ void chunk_attn_fwd_f32<64>(KernelArgs);
 
 // The clears before a key-split launch in one kernel: the nq claim words of
 // the work-queue slot and the ncnt arrival counters of the split items (one
@@ -397,11 +399,23 @@ hipError_t launch_t(const KernelArgs& a, int n_persist, int n_cu, hipStream_t st
 template <int W>
 hipError_t launch_w(const KernelArgs& a, int n_persist, int n_cu, int head_dim, int dtype,
                     hipStream_t stream) {
+  (void)dtype;  // bf16 only: fp32 calls run launch_f32
+  if (head_dim == 128) return launch_t<128, __bf16, W>(a, n_persist, n_cu, stream);
+  return launch_t<64, __bf16, W>(a, n_persist, n_cu, stream);
+}
+
+// fp32 calls: one workgroup of 4 waves per 64-row item, fp32 throughout (no
+// work queue, no recheck: the softmax keeps a running maximum).
+hipError_t launch_f32(const KernelArgs& a, int head_dim, hipStream_t stream) {
+  if (a.plan.n_items < 1) return hipSuccess;
+  const dim3 grid((unsigned)a.plan.n_items);
   if (head_dim == 128)
-    return dtype == CHUNKATTN_BF16 ? launch_t<128, __bf16, W>(a, n_persist, n_cu, stream)
-                                   : launch_t<128, float, W>(a, n_persist, n_cu, stream);
-  return dtype == CHUNKATTN_BF16 ? launch_t<64, __bf16, W>(a, n_persist, n_cu, stream)
-                                 : launch_t<64, float, W>(a, n_persist, n_cu, stream);
+    hipLaunchKernelGGL(chunkattn::chunk_attn_fwd_f32<128>, grid, dim3(256),
+                       chunkattn::kF32LdsBytes<128>, stream, a);
+  else
+    hipLaunchKernelGGL(chunkattn::chunk_attn_fwd_f32<64>, grid, dim3(256),
+                       chunkattn::kF32LdsBytes<64>, stream, a);
+  return hipGetLastError();
 }
 
 // The 384-row main pass (48 rows per wave, persistent like the 256-row one):
@@ -437,6 +451,7 @@ hipError_t launch_wide(const KernelArgs& a, const KernelArgs& blocks, int n_pers
 
 hipError_t launch(const KernelArgs& a, const KernelArgs& blocks, int block_rows, int n_persist,
                   int n_cu, int head_dim, int dtype, bool exact, hipStream_t stream) {
+  if (block_rows == chunkattn::kF32BlockRows) return launch_f32(a, head_dim, stream);
   if (block_rows == 384) return launch_wide(a, blocks, n_persist, n_cu, exact, stream);
   return block_rows == 128 ? launch_w<4>(a, n_persist, n_cu, head_dim, dtype, stream)
                            : launch_w<8>(a, n_persist, n_cu, head_dim, dtype, stream);
@@ -701,13 +716,14 @@ int chunkattn_create(chunkattn_ctx** out, int device_ordinal, unsigned flags) {
     }
     ctx->static_scratch = static_cast<unsigned long long*>(p);
     if (allow_wide_lds() != hipSuccess || allow_pingpong_lds<128, __bf16>() != hipSuccess ||
-        allow_pingpong_lds<128, float>() != hipSuccess ||
         allow_pingpong_lds<64, __bf16>() != hipSuccess ||
-        allow_pingpong_lds<64, float>() != hipSuccess) {
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&chunkattn::chunk_attn_fwd_f32<128>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)chunkattn::kF32LdsBytes<128>) != hipSuccess) {
       if (ctx->queue) (void)hipFree(ctx->queue);
       delete ctx;
       return set_err(&g_thread_err, CHUNKATTN_EDEVICE,
-                     "device %d: cannot raise the LDS limit of the 256-row kernels",
+                     "device %d: cannot raise the LDS limit of the main kernels",
                      device_ordinal);
     }
   }

@@ -30,26 +30,30 @@
  *   kv_cache     : [n_chunks][2][chunk_len][heads][head_dim]; slot c holds the
  *                  predecessor's K (index 0) then V (index 1); slot 0 is never read.
  *
- * Numerics.  Q.K^T and P.V run on bf16 matrix cores with fp32 accumulation and
- * an fp32 softmax; P is rounded to bf16 before the P.V product and the
- * softmax denominator is summed from the same rounded P, so a constant V comes
- * back bit-exactly.  With 256- and 384-row work items Q is multiplied by scale * log2 e
- * and rounded to bf16 once per item (relative 2^-9 per element).  dtype F32 means fp32
- * storage in and out, rounded to bf16 (nearest-even) on load.  bf16 outputs are
- * rounded nearest-even.  Results are bitwise deterministic run to run, and the
+ * Numerics.  bf16 calls: Q.K^T and P.V run on bf16 matrix cores with fp32
+ * accumulation and an fp32 softmax; P is rounded to bf16 before the P.V
+ * product and the softmax denominator is summed from the same rounded P, so a
+ * constant V comes back bit-exactly.  With 256- and 384-row work items Q is
+ * multiplied by scale * log2 e and rounded to bf16 once per item (relative
+ * 2^-9 per element).  bf16 outputs are rounded nearest-even.  fp32 calls
+ * (dtype F32) keep fp32 throughout: fp32 matrix cores, an fp32 softmax with a
+ * running maximum, fp32 output (64-row work items; the fp32 matrix-core peak
+ * is a sixteenth of the bf16 one).  Results are bitwise deterministic run to run, and the
  * separate-cache and in-place-predecessor forms give bitwise-equal outputs.
  *
  * Ownership and asynchrony.  Every tensor pointer is device memory owned by the
  * caller and must stay valid until the stream work completes.  The library
- * owns only the context; a context of 256-row work items also owns a 64 KB
- * device buffer, 512 work-queue slots of its persistent main pass, allocated
- * by chunkattn_create.  queue_step and full make no allocation: they
- * validate, enqueue the kernels on hip_stream (NULL = the legacy default
- * stream) and return; a device fault surfaces at the caller's next
- * synchronisation.  One context may be used by one host thread at a time;
- * separate contexts are independent.  Each call of a 256-row context uses one
- * work-queue slot, which a small kernel on hip_stream clears right before the
- * main pass.  Eager calls take the next of 64 slots in turn: calls may be
+ * owns only the context; a context also owns a 64 KB device buffer, 512
+ * work-queue slots of its persistent main passes (256- and 384-row items),
+ * allocated by chunkattn_create, and a stream-ordered memory pool from which a
+ * launch with few items per CU takes the workspace of its key-axis split (see
+ * chunkattn_ctx_set_tail_split; the pool keeps its memory, so a call
+ * allocates only while the pool grows).  The calls validate, enqueue the
+ * kernels on hip_stream (NULL = the legacy default stream) and return; a
+ * device fault surfaces at the caller's next synchronisation.  One context may
+ * be used by one host thread at a time; separate contexts are independent.
+ * Each call with a persistent main pass uses one work-queue slot, which a
+ * small kernel on hip_stream clears right before the main pass.  Eager calls take the next of 64 slots in turn: calls may be
  * spread over several streams as long as at most 64 of them are in flight at
  * once (calls on one stream never overlap).  A call made while hip_stream is
  * being captured into a graph gets a slot of its own (at most 448 such calls
@@ -86,13 +90,13 @@ typedef enum {
 
 typedef enum {
     CHUNKATTN_BF16 = 0, /* bf16 storage in and out */
-    CHUNKATTN_F32 = 1   /* fp32 storage in and out (operands rounded to bf16) */
+    CHUNKATTN_F32 = 1   /* fp32 storage in and out, fp32 arithmetic */
 } chunkattn_dtype;
 
-/* chunkattn_create flags: query rows per work item (one workgroup).  With no
- * flag (0) a context uses 384-row items for bf16, head_dim-128 calls and
- * 256-row items for every other call; CHUNKATTN_FLAG_BLOCK384 asks for the
- * same explicitly. */
+/* chunkattn_create flags: query rows per work item (one workgroup) of bf16
+ * calls.  With no flag (0) a context uses 384-row items for head_dim-128 calls
+ * and 256-row items for head_dim 64; CHUNKATTN_FLAG_BLOCK384 asks for the same
+ * explicitly.  fp32 calls always use 64-row items on the fp32 kernel. */
 #define CHUNKATTN_FLAG_BLOCK128 1u /* 128 rows, 4 waves, two workgroups per CU */
 #define CHUNKATTN_FLAG_BLOCK256 2u /* 256 rows, 8 waves of 32 rows, one workgroup per CU */
 #define CHUNKATTN_FLAG_BLOCK384 4u /* 384 rows, 8 waves of 48 rows, one workgroup per CU,
@@ -129,7 +133,7 @@ int chunkattn_create(chunkattn_ctx **out, int device_ordinal, unsigned flags);
 int chunkattn_ctx_block_rows(const chunkattn_ctx *ctx);
 
 /* Query rows per work item of this context for a call with the given
- * head_dim and dtype. */
+ * head_dim and dtype (64 for every fp32 call). */
 int chunkattn_ctx_call_block_rows(const chunkattn_ctx *ctx, int head_dim, int dtype);
 
 /* 384-row query blocks per work item of the context's calls that use 384-row

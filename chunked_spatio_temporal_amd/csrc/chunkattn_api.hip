@@ -104,11 +104,11 @@ constexpr int kMaxSplitParts = 8;
 
 // Key-axis split of the last items of a launch with one 384-row block per
 // item: {items, parts}, {0, 0} for none.  When a launch has few items per CU
-// (fewer than 8), the last wave of items decides when it ends: the last items
-// in work order are cut into 4 parts each, so the end of the launch is made of
-// quarter items.  How many: n_cu below 3 items per CU, 1.5 n_cu from 3 to 7
-// (measured best of n_cu/2..2.7 n_cu and 2, 4 and 8 parts on the 5-head and
-// 12-head 480p queues; 2 parts gained about half as much).  Every part walks
+// (fewer than 8), the last wave of items decides when it ends: the last long
+// items (plan_with_split) are cut along their keys, so the end of the launch is
+// made of part items.  Below 3 items per CU, 2/3 n_cu items into 2 parts; from
+// 3 to 7, n_cu items into 4 parts (measured best of 1/2..2.7 n_cu items and 2,
+// 3, 4 and 8 parts on the 5-head and 12-head 480p queues).  Every part walks
 // at least one key tile.
 struct SplitChoice {
   int64_t items;
@@ -131,8 +131,8 @@ SplitChoice split_choice(const chunkattn_ctx* ctx, const Plan& p) {
   } else {
     const int64_t per_cu = p.n_items / (ctx->n_cu > 0 ? ctx->n_cu : 1);
     if (per_cu >= 8) return {0, 0};
-    items = per_cu < 3 ? ctx->n_cu : ctx->n_cu * 3 / 2;
-    parts = 4;
+    items = per_cu < 3 ? ctx->n_cu * 2 / 3 : ctx->n_cu;
+    parts = per_cu < 3 ? 2 : 4;
   }
   if (parts > min_tiles) parts = min_tiles;
   if (parts < 2) return {0, 0};
@@ -427,7 +427,7 @@ hipError_t launch_wide(const KernelArgs& a, const KernelArgs& blocks, int n_pers
                        bool exact, hipStream_t stream) {
   if (!a.queue || n_persist < 1 || a.plan.n_xcd > kQueueWords) return hipErrorInvalidValue;
   if (a.plan.split_parts > 1) {
-    const int64_t n = a.plan.n_items - a.plan.split_from;
+    const int64_t n = a.plan.split_count;
     hipLaunchKernelGGL(chunkattn::split_launch_clear, dim3((unsigned)((n + 255) / 256)),
                        dim3(256), 0, stream, a.queue, a.plan.n_xcd, a.split_cnt, n);
   } else {

@@ -51,12 +51,13 @@ struct Plan {
   int n_xcd;       // dies for the launch-order renumbering (>= 1)
   int64_t n_items;
   int64_t n_items_pred;  // items of entries with a predecessor (scheduled first)
-  // Key-axis split of the last items (split_parts = 1: none).  Items
-  // [split_from, n_items) of the work order are each cut into split_parts
-  // units along their key tiles; the launch runs n_units units.
+  // Key-axis split (split_parts = 1: none).  Items [split_from, split_from +
+  // split_count) of the work order are each cut into split_parts units along
+  // their key tiles; the launch runs n_units units.
   int64_t split_from;
   int split_parts;
   int64_t n_units;
+  int64_t split_count;
 };
 
 struct Item {
@@ -89,17 +90,24 @@ CA_HD Plan make_plan(int n_batch, int first_pred, int heads, int lq, int lown, i
   p.split_from = p.n_items;
   p.split_parts = 1;
   p.n_units = p.n_items;
+  p.split_count = 0;
   return p;
 }
 
-// The same plan with its last n_split items (work order) cut into `parts`
-// units each along the key axis.
+// The same plan with n_split items cut into `parts` units each along the key
+// axis: the last n_split items of the long group (entries with a
+// predecessor) when the plan has one, else the last n_split of the work order.
+// The short items then stay whole: they cost a fraction of a long item and
+// fill the end of the launch better than quarter units of themselves, whose
+// start and finish would weigh as much as their few tiles.
 CA_HD Plan plan_with_split(Plan p, int64_t n_split, int parts) {
-  if (n_split > p.n_items) n_split = p.n_items;
+  const int64_t group_end = p.n_items_pred > 0 ? p.n_items_pred : p.n_items;
+  if (n_split > group_end) n_split = group_end;
   if (parts < 2 || n_split <= 0) return p;
-  p.split_from = p.n_items - n_split;
+  p.split_from = group_end - n_split;
+  p.split_count = n_split;
   p.split_parts = parts;
-  p.n_units = p.split_from + n_split * parts;
+  p.n_units = p.n_items + n_split * (parts - 1);
   return p;
 }
 // Every entry the same size.
@@ -195,12 +203,15 @@ CA_HD Item decode(const Plan& p, int64_t w) {
 }
 
 // Work unit u of a plan with a key-axis split: units [0, split_from) are the
-// items themselves; unit split_from + s is part s % split_parts of item
-// split_from + s / split_parts, whose key tiles [T*part/parts, T*(part+1)/parts)
-// it walks (T: the item's tiles).
+// items themselves; unit split_from + s (s < split_count * split_parts) is
+// part s % split_parts of item split_from + s / split_parts, whose key tiles
+// [T*part/parts, T*(part+1)/parts) it walks (T: the item's tiles); the units
+// after those are the items after the split range, whole.
 CA_HD Item decode_unit(const Plan& p, int64_t u) {
   if (u < p.split_from) return decode(p, u);
   const int64_t s = u - p.split_from;
+  const int64_t su = p.split_count * p.split_parts;
+  if (s >= su) return decode(p, p.split_from + p.split_count + (s - su));
   Item it = decode(p, p.split_from + s / p.split_parts);
   const int part = (int)(s % p.split_parts);
   const int t = it.t_hi;
@@ -213,15 +224,17 @@ CA_HD Item decode_unit(const Plan& p, int64_t u) {
 
 // Persistent claim over units.  Without a split it is claim_word_item.  With
 // one, die x's queue holds its even share of the unsplit long items, then of
-// the unsplit short items, then of the split units (each a contiguous range),
-// so the small units come last on every die.
+// the unsplit short items before the split range and after it, then of the
+// split units (each a contiguous range of units), so the small units come
+// last on every die.
 CA_HD int64_t claim_word_unit(const Plan& p, int x, unsigned long long old) {
   if (p.split_parts <= 1) return claim_word_item(p, x, old);
   const int64_t a = p.n_items_pred < p.split_from ? p.n_items_pred : p.split_from;
-  const int64_t sizes[3] = {a, p.split_from - a, p.n_units - p.split_from};
-  const int64_t starts[3] = {0, a, p.split_from};
+  const int64_t su_end = p.split_from + p.split_count * p.split_parts;
+  const int64_t sizes[4] = {a, p.split_from - a, p.n_units - su_end, su_end - p.split_from};
+  const int64_t starts[4] = {0, a, su_end, p.split_from};
   int64_t pos = (int64_t)old;
-  for (int k = 0; k < 3; ++k) {
+  for (int k = 0; k < 4; ++k) {
     const int64_t s0 = die_share_start(sizes[k], x, p.n_xcd);
     const int64_t cnt = die_share_start(sizes[k], x + 1, p.n_xcd) - s0;
     if (pos < cnt) return starts[k] + s0 + pos;

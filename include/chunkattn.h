@@ -149,14 +149,18 @@ int chunkattn_ctx_set_item_blocks(chunkattn_ctx *ctx, int blocks);
 
 /* Key-axis split of the last work items of the context's calls with one
  * 384-row block per item.  A launch with few items per CU ends when its last
- * items do; cutting the last `items` items (in work order) into `parts` ranges
- * of their key tiles lets the CUs finish together.  Each part stores its
+ * items do; cutting `items` items into `parts` ranges of their key tiles lets
+ * the CUs finish together.  The items cut are the last of those with a
+ * predecessor segment (the long ones; the short items of the queue's first
+ * chunk stay whole and run before the parts), or the last of the launch when
+ * no item has a predecessor.  Each part stores its
  * unnormalised O and row sums l (the softmax has no maximum, so the parts add
  * exactly up to fp32 rounding order) in a workspace taken from a
  * stream-ordered memory pool of the context, and the last part to finish adds
  * the others and writes the output.  items = -1 (the default): chosen per
- * call when a launch has fewer than 8 items per CU: the last n_CU items (1.5
- * n_CU from 3 items per CU up) into 4 parts); 0: never; > 0: that many items, with
+ * call when a launch has fewer than 8 items per CU (2/3 n_CU items into 2
+ * parts below 3 items per CU, n_CU items into 4 parts from 3 up); 0: never;
+ * > 0: that many items, with
  * parts in [2, 8] (fewer if an item has fewer key tiles).  Never used under
  * graph capture or by chunkattn_queue_step_noalloc.  CHUNKATTN_EINVAL
  * otherwise.  Not thread-safe against concurrent calls on the same context. */

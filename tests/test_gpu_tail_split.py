@@ -1,7 +1,10 @@
 """Key-axis split of the last work items (384-row items, one block each).
 
 A launch with few items per CU ends when its last items do, so those items
-may be cut into parts along their key tiles.  The softmax carries no maximum,
+may be cut into parts along their key tiles: the last items with a
+predecessor segment in a queue step (the short items of the first chunk stay
+whole), the last items of the launch when none has one.  The softmax carries
+no maximum,
 so the parts' unnormalised outputs and row sums add: O = sum_p O_p / sum_p l_p
 (the same numerators, summed in another fp32 order).  Each part stores its
 partial in a workspace; the part that finishes last adds all of them in part
@@ -132,3 +135,27 @@ def test_short_launch_default_splits_match_oracle():
     cache = synth.build_cache(k, v)
     out = run(ca.create(0), q, k, v, cache)
     assert_parity(to_f64(out), oracle.queue_step(q, k, v, cache), "default split")
+
+
+def test_split_without_predecessor_group():
+    """Full attention (no item has a predecessor segment): the split takes the
+    last items of the launch.  2 x 1000 query rows over 1000 keys, one block per
+    item, the last 4 items in 3 parts: every element against the oracle and
+    within 2e-3 of the unsplit launch."""
+    B, lq, lkv, H, D = 2, 1000, 1000, 2, 128
+    q = synth.normal((B, lq, H, D), 606, synth.Q_ID, DEV)
+    k = synth.normal((B, lkv, H, D), 606, synth.K_ID, DEV)
+    v = synth.normal((B, lkv, H, D), 606, synth.V_ID, DEV)
+    outs = []
+    for items, parts in ((4, 3), (0, 0)):
+        c = ca.Context(0, 0)
+        c.set_item_blocks(1)
+        c.set_tail_split(items, parts)
+        out = torch.full_like(q, SENTINEL)
+        ca.full(q, k, v, out=out, ctx=c)
+        torch.cuda.synchronize()
+        outs.append(out)
+    ref = oracle.full(q, k, v)
+    assert_parity(to_f64(outs[0]), ref, "full split")
+    d = error_stats(to_f64(outs[0]), to_f64(outs[1]))
+    assert d["max_abs"] <= 2e-3 and d["mean_abs"] <= 2e-5, d

@@ -56,3 +56,20 @@ def test_noalloc_validates_like_queue_step():
     with pytest.raises(ca.ChunkAttnError) as e:
         ca.queue_step_noalloc(q, k, v, None, torch.empty_like(q))
     assert e.value.status == ca.EUNSUPPORTED
+
+
+def test_noalloc_fp32_matches_queue_step():
+    """fp32 calls run the fp32 kernel, one workgroup per item and no work
+    queue: the allocation-free entry point gives the same bits."""
+    ctx = ca.Context(0, 0)
+    for (n, L, H, D, seed) in [(4, 300, 3, 64, 63), (2, 129, 2, 128, 64)]:
+        print("case noalloc fp32", (n, L, H, D), flush=True)
+        q, k, v = synth.queue_inputs(n, L, H, D, seed=seed, device=DEV, dtype=torch.float32)
+        cache = synth.build_cache(k, v)
+        ref = torch.full_like(q, UNWRITTEN)
+        ca.queue_step(q, k, v, cache, out=ref, ctx=ctx)
+        got = torch.full_like(q, UNWRITTEN)
+        ca.queue_step_noalloc(q, k, v, cache, got, ctx=ctx)
+        torch.cuda.synchronize()
+        assert torch.isfinite(ref).all() and (ref.abs() < 2.0 ** 99).all()
+        assert torch.equal(got, ref), f"noalloc differs from queue_step at {(n, L, H, D)}"

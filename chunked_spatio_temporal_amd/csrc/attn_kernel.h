@@ -39,8 +39,8 @@
 // address map realises a 16-byte-block XOR swizzle.  Tiles inside one segment
 // use a wave-uniform base address plus a fixed per-lane 32-bit offset; only
 // the tile that straddles the predecessor/own boundary and the ragged last
-// tile compute per-lane row addresses.  fp32 inputs are converted to bf16 in
-// registers on the way (same LDS layout).  Q stays in registers throughout.
+// tile compute per-lane row addresses.  Q stays in registers throughout.
+// (fp32 storage runs its own kernel, attn_f32.h.)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -121,21 +121,6 @@ struct Io<__bf16> {
   static __device__ __forceinline__ void store4(__bf16* p, float a, float b, float c, float d) {
     u32x2_t w = {pack_bf16(a, b), pack_bf16(c, d)};
     *reinterpret_cast<u32x2_t*>(p) = w;
-  }
-};
-
-template <>
-struct Io<float> {
-  static __device__ __forceinline__ u32x4_t load8(const float* p) {
-    const f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[0];
-    const f32x4_t b = reinterpret_cast<const f32x4_t*>(p)[1];
-    u32x4_t r = {pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(b[0], b[1]),
-                 pack_bf16(b[2], b[3])};
-    return r;
-  }
-  static __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
-    f32x4_t w = {a, b, c, d};
-    *reinterpret_cast<f32x4_t*>(p) = w;
   }
 };
 
@@ -320,6 +305,7 @@ __device__ __forceinline__ void attn_item_sync(const KernelArgs& a, const Item& 
                                                unsigned char* smem) {
   using G = Geo<D>;
   constexpr int kCpw = G::kChunks / W;  // 1 KB load chunks per wave per matrix
+  static_assert(sizeof(T) == 2, "bf16 storage (fp32 calls run attn_f32.h)");
   static_assert(kCpw * W == G::kChunks, "tile split across waves");
 
   const int tid = threadIdx.x;
@@ -374,39 +360,21 @@ __device__ __forceinline__ void attn_item_sync(const KernelArgs& a, const Item& 
   auto load_tile = [&](int t, unsigned char* kb) __attribute__((always_inline)) {
     unsigned char* vb = kb + G::kTileBytes;
     const int r0 = t * kBN;
-    if constexpr (sizeof(T) == 2) {
-      if (r0 + kBN <= pred || (r0 >= pred && r0 + kBN <= total)) {
-        // whole tile in one segment: uniform base + fixed per-lane offsets
-        const bool in_pred = r0 + kBN <= pred;
-        const int64_t row = in_pred ? r0 : r0 - pred;
-        const char* kbase = reinterpret_cast<const char*>((in_pred ? kpre : kown) + row * rs);
-        const char* vbase = reinterpret_cast<const char*>((in_pred ? vpre : vown) + row * rs);
+    if (r0 + kBN <= pred || (r0 >= pred && r0 + kBN <= total)) {
+      // whole tile in one segment: uniform base + fixed per-lane offsets
+      const bool in_pred = r0 + kBN <= pred;
+      const int64_t row = in_pred ? r0 : r0 - pred;
+      const char* kbase = reinterpret_cast<const char*>((in_pred ? kpre : kown) + row * rs);
+      const char* vbase = reinterpret_cast<const char*>((in_pred ? vpre : vown) + row * rs);
 #pragma unroll
-        for (int i = 0; i < kCpw; ++i) {
-          const int c = wave * kCpw + i;
-          load_lds16(kbase + koffs[i], kb + c * 1024);
-          load_lds16(vbase + voffs[i], vb + c * 1024);
-        }
-      } else {
-        // straddling or ragged tile: per-lane row select; rows past the end
-        // re-read the last row (their scores are masked, their P is zero)
-#pragma unroll
-        for (int i = 0; i < kCpw; ++i) {
-          const int c = wave * kCpw + i;
-          const int r = lrow(i);
-          int j = r0 + r;
-          j = j < total ? j : total - 1;
-          const int pb = lane % G::kBlk;
-          const int kblk = pb ^ k_swz<D>(r);
-          const int vblk = pb ^ v_swz<D>(r);
-          const T* kr = j < pred ? kpre + j * rs : kown + (j - pred) * rs;
-          const T* vr = j < pred ? vpre + j * rs : vown + (j - pred) * rs;
-          load_lds16(kr + kblk * 8, kb + c * 1024);
-          load_lds16(vr + vblk * 8, vb + c * 1024);
-        }
+      for (int i = 0; i < kCpw; ++i) {
+        const int c = wave * kCpw + i;
+        load_lds16(kbase + koffs[i], kb + c * 1024);
+        load_lds16(vbase + voffs[i], vb + c * 1024);
       }
     } else {
-      // fp32 storage: convert to bf16 in registers, store with the same layout
+      // straddling or ragged tile: per-lane row select; rows past the end
+      // re-read the last row (their scores are masked, their P is zero)
 #pragma unroll
       for (int i = 0; i < kCpw; ++i) {
         const int c = wave * kCpw + i;
@@ -414,12 +382,12 @@ __device__ __forceinline__ void attn_item_sync(const KernelArgs& a, const Item& 
         int j = r0 + r;
         j = j < total ? j : total - 1;
         const int pb = lane % G::kBlk;
+        const int kblk = pb ^ k_swz<D>(r);
+        const int vblk = pb ^ v_swz<D>(r);
         const T* kr = j < pred ? kpre + j * rs : kown + (j - pred) * rs;
         const T* vr = j < pred ? vpre + j * rs : vown + (j - pred) * rs;
-        const u32x4_t kv = Io<T>::load8(kr + (pb ^ k_swz<D>(r)) * 8);
-        const u32x4_t vv = Io<T>::load8(vr + (pb ^ v_swz<D>(r)) * 8);
-        *reinterpret_cast<u32x4_t*>(kb + c * 1024 + lane * 16) = kv;
-        *reinterpret_cast<u32x4_t*>(vb + c * 1024 + lane * 16) = vv;
+        load_lds16(kr + kblk * 8, kb + c * 1024);
+        load_lds16(vr + vblk * 8, vb + c * 1024);
       }
     }
   };

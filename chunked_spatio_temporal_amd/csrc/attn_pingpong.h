@@ -109,6 +109,7 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
   constexpr int W = 8;
   constexpr int kCpw = G::kChunks / W;  // 1 KB load chunks per wave per matrix
   static_assert(kCpw >= 1 && kCpw * W == G::kChunks, "tile split across waves");
+  static_assert(sizeof(T) == 2, "bf16 storage (fp32 calls run attn_f32.h)");
   constexpr int kKs = D / 16;
   constexpr int kDb = D / 32;
   constexpr int kStepsQK = 2 * kKs;              // 2 key blocks x k-steps
@@ -203,33 +204,20 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
     const T* pre = kV ? vpre : kpre;
     const T* own = kV ? vown : kown;
     const int r0 = t * kBN;
-    if constexpr (sizeof(T) == 2) {
-      if (t < np || (t >= no && t < nf)) {
-        const uint64_t b = (t < np ? (kV ? vpre_b : kpre_b) : (kV ? vown_s : kown_s)) +
-                           (uint64_t)(uint32_t)t * tstride;
-        const char* base = reinterpret_cast<const char*>((uintptr_t)b);
-        if constexpr (kCpw == 2) {
-          load_lds16x2_async(base, kV ? voffs[0] : koffs[0], kV ? voffs[1] : koffs[1],
-                             dst + wave * kCpw * 1024);
-        } else {
-#pragma unroll
-          for (int i = 0; i < kCpw; ++i)
-            load_lds16_async(base, kV ? voffs[i] : koffs[i], dst + (wave * kCpw + i) * 1024);
-        }
+    if (t < np || (t >= no && t < nf)) {
+      const uint64_t b = (t < np ? (kV ? vpre_b : kpre_b) : (kV ? vown_s : kown_s)) +
+                         (uint64_t)(uint32_t)t * tstride;
+      const char* base = reinterpret_cast<const char*>((uintptr_t)b);
+      if constexpr (kCpw == 2) {
+        load_lds16x2_async(base, kV ? voffs[0] : koffs[0], kV ? voffs[1] : koffs[1],
+                           dst + wave * kCpw * 1024);
       } else {
-        // straddling or ragged tile: rows past the end re-read the last row
 #pragma unroll
-        for (int i = 0; i < kCpw; ++i) {
-          const int r = lrow(i);
-          int j = r0 + r;
-          j = j < total ? j : total - 1;
-          const int blk = (lane % G::kBlk) ^ (kV ? v_swz<D>(r) : k_swz<D>(r));
-          const T* src = j < pred ? pre + (int64_t)j * rs : own + (int64_t)(j - pred) * rs;
-          load_lds16_async(src + blk * 8, dst + (wave * kCpw + i) * 1024);
-        }
+        for (int i = 0; i < kCpw; ++i)
+          load_lds16_async(base, kV ? voffs[i] : koffs[i], dst + (wave * kCpw + i) * 1024);
       }
     } else {
-      // fp32 storage: convert to bf16 in registers, same LDS layout
+      // straddling or ragged tile: rows past the end re-read the last row
 #pragma unroll
       for (int i = 0; i < kCpw; ++i) {
         const int r = lrow(i);
@@ -237,8 +225,7 @@ __device__ __forceinline__ void attn_item_pingpong(const KernelArgs& a, const It
         j = j < total ? j : total - 1;
         const int blk = (lane % G::kBlk) ^ (kV ? v_swz<D>(r) : k_swz<D>(r));
         const T* src = j < pred ? pre + (int64_t)j * rs : own + (int64_t)(j - pred) * rs;
-        *reinterpret_cast<u32x4_t*>(dst + (wave * kCpw + i) * 1024 + lane * 16) =
-            Io<T>::load8(src + blk * 8);
+        load_lds16_async(src + blk * 8, dst + (wave * kCpw + i) * 1024);
       }
     }
   };

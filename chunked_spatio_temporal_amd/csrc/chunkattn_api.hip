@@ -702,7 +702,7 @@ int chunkattn_create(chunkattn_ctx** out, int device_ordinal, unsigned flags) {
   }
   {
     // the noalloc entry point's static scratch on this device, and the LDS
-    // limit of the 256-row kernels, set up once here so that hot calls do
+    // limit of the main kernels, set up once here so that hot calls do
     // neither
     DeviceGuard g(device_ordinal);
     void* p = nullptr;

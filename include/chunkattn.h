@@ -124,7 +124,8 @@ int chunkattn_block_rows(void);
  * optionally or-ed with CHUNKATTN_FLAG_EXACT_SCALE; results do not depend on
  * the work-item size beyond fp32 rounding order.  On success *out owns the context; release it
  * with chunkattn_destroy.  CHUNKATTN_EDEVICE also reports a failed allocation
- * of the work queue (256-row contexts).
+ * of the work queue (every context but a 128-row one: the 256- and 384-row
+ * main passes are persistent).
  */
 int chunkattn_create(chunkattn_ctx **out, int device_ordinal, unsigned flags);
 

@@ -90,29 +90,27 @@ __device__ __forceinline__ void store_device16(float* p, const f32x4_t& x) {
 __device__ __forceinline__ void store_device4(float* p, float x) {
   asm volatile("global_store_dword %0, %1, off sc1" : : "v"(p), "v"(x) : "memory");
 }
-// eight 16-byte loads at p, p + stride, ... (stride in floats)
-__device__ __forceinline__ void load_device16x8(const float* p, int stride, f32x4_t (&x)[8]) {
+// eight 16-byte loads at p, p + 1 KB, ... p + 7 KB and one 4-byte load at
+// pl, all in flight together (one memory latency); two base addresses with
+// immediate offsets keep the address registers few
+__device__ __forceinline__ void load_device16x8_4(const float* p, f32x4_t (&x)[8],
+                                                  const float* pl, float& l) {
+  const float* p4 = p + 1024;  // + 4 KB
   asm volatile(
-      "global_load_dwordx4 %0, %8, off sc1\n\t"
-      "global_load_dwordx4 %1, %9, off sc1\n\t"
-      "global_load_dwordx4 %2, %10, off sc1\n\t"
-      "global_load_dwordx4 %3, %11, off sc1\n\t"
-      "global_load_dwordx4 %4, %12, off sc1\n\t"
-      "global_load_dwordx4 %5, %13, off sc1\n\t"
-      "global_load_dwordx4 %6, %14, off sc1\n\t"
-      "global_load_dwordx4 %7, %15, off sc1\n\t"
+      "global_load_dwordx4 %0, %9, off sc1\n\t"
+      "global_load_dwordx4 %1, %9, off offset:1024 sc1\n\t"
+      "global_load_dwordx4 %2, %9, off offset:2048 sc1\n\t"
+      "global_load_dwordx4 %3, %9, off offset:3072 sc1\n\t"
+      "global_load_dwordx4 %4, %10, off sc1\n\t"
+      "global_load_dwordx4 %5, %10, off offset:1024 sc1\n\t"
+      "global_load_dwordx4 %6, %10, off offset:2048 sc1\n\t"
+      "global_load_dwordx4 %7, %10, off offset:3072 sc1\n\t"
+      "global_load_dword %8, %11, off sc1\n\t"
       "s_waitcnt vmcnt(0)"
       : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
-        "=&v"(x[6]), "=&v"(x[7])
-      : "v"(p), "v"(p + stride), "v"(p + 2 * stride), "v"(p + 3 * stride),
-        "v"(p + 4 * stride), "v"(p + 5 * stride), "v"(p + 6 * stride), "v"(p + 7 * stride)
+        "=&v"(x[6]), "=&v"(x[7]), "=&v"(l)
+      : "v"(p), "v"(p4), "v"(pl)
       : "memory");
-}
-__device__ __forceinline__ float load_device4(const float* p) {
-  float x;
-  asm volatile("global_load_dword %0, %1, off sc1\n\ts_waitcnt vmcnt(0)" : "=&v"(x) : "v"(p)
-               : "memory");
-  return x;
 }
 
 __device__ __forceinline__ void pin(f32x4_t& x) { asm volatile("" : "+v"(x)); }
@@ -707,19 +705,22 @@ __device__ __forceinline__ void attn_item_wide(const KernelArgs& a, const Item& 
       wg_barrier();
       if (range_flags[2] == 0) return;
       // all parts, the own one read back too, added in part order: the sum
-      // does not depend on which part arrived last
+      // does not depend on which part arrived last.  A block's O and l of one
+      // part come in one batch of loads (8 dim blocks of 64 * 4 floats, 1 KB
+      // apart, and l): one memory latency per part and block.
       for (int p = 0; p < parts; ++p) {
         const float* ws = slot_of(p);
 #pragma unroll
         for (int q3 = 0; q3 < kQB; ++q3) {
           f32x4_t x[kDB];
-          load_device16x8(ws + ((wave * 3 + q3) * kDB * 64 + l6) * 4, 64 * 4, x);
+          float lp;
+          load_device16x8_4(ws + ((wave * 3 + q3) * kDB * 64 + l6) * 4, x,
+                            ws + kSplitOFloats + (wave * 3 + q3) * 64 + l6, lp);
 #pragma unroll
           for (int db = 0; db < kDB; ++db)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               oacc[q3][db][e] = p == 0 ? x[db][e] : oacc[q3][db][e] + x[db][e];
-          const float lp = load_device4(ws + kSplitOFloats + (wave * 3 + q3) * 64 + l6);
           l_last[q3] = p == 0 ? lp : l_last[q3] + lp;
         }
       }

@@ -566,6 +566,7 @@ int run(chunkattn_ctx* ctx, const KernelArgs& args, int head_dim, int dtype, voi
       const Plan& p = a.plan;
       main.plan = chunkattn::make_plan(p.n_batch, p.first_pred, p.heads, p.lq, p.lown, p.lpred,
                                        nb * bm, p.n_xcd, p.lq_last, p.lown_last);
+      if (p.head_major) main.plan = chunkattn::plan_head_major(main.plan);
     }
   }
   // One block per item, few items per CU: cut the last items along the keys.
@@ -853,6 +854,8 @@ int chunkattn_full(chunkattn_ctx* ctx, const void* q, const void* k, const void*
   a.q_bstride = (int64_t)lq * heads * head_dim;
   a.o_bstride = a.q_bstride;
   a.kv_bstride = kv_batch_stride;
+  // every entry reads one K/V: run the items of one head together
+  if (kv_batch_stride == 0) a.plan = chunkattn::plan_head_major(a.plan);
   a.p_bstride = 0;
   a.pred_shift = 0;
   a.row_stride = heads * head_dim;

@@ -14,6 +14,12 @@
 // queue step) come first, because they walk the most key rows; entries without
 // one (chunk 0) fill the tail of the launch.  Within a group the order is
 // (b, h, t) with t fastest, so consecutive items share one chunk/head's K/V.
+// A plan of one group whose entries are all the same size may run its items
+// head-major instead, (h, b, t) (plan_head_major): when every entry attends
+// over one shared K/V (per-chunk cross-attention to the text tokens), the
+// items a die runs at one time then read one head's K/V rather than one per
+// concurrent (b, h).  The work index, which decode() takes, stays (b, h, t);
+// plan_slot_work() maps launch positions onto it in the plan's order.
 //
 // Die-aware launch order.  Workgroup ids are handed to the accelerator dies
 // round-robin (id % n_xcd), and each die runs its own ids in increasing order.
@@ -58,6 +64,7 @@ struct Plan {
   int split_parts;
   int64_t n_units;
   int64_t split_count;
+  int head_major;  // 1: items run in (h, b, t) order (plan_head_major)
 };
 
 struct Item {
@@ -91,6 +98,17 @@ CA_HD Plan make_plan(int n_batch, int first_pred, int heads, int lq, int lown, i
   p.split_parts = 1;
   p.n_units = p.n_items;
   p.split_count = 0;
+  p.head_major = 0;
+  return p;
+}
+
+// The same plan run head-major when it has one group (no predecessor
+// segments), every entry the same size and fewer than 2^31 items (the order
+// map divides in 32 bits); otherwise unchanged.
+CA_HD Plan plan_head_major(Plan p) {
+  if (p.first_pred >= p.n_batch && p.lq_last == p.lq && p.lown_last == p.lown &&
+      p.n_items <= 0x7fffffff)
+    p.head_major = 1;
   return p;
 }
 
@@ -104,6 +122,7 @@ CA_HD Plan plan_with_split(Plan p, int64_t n_split, int parts) {
   const int64_t group_end = p.n_items_pred > 0 ? p.n_items_pred : p.n_items;
   if (n_split > group_end) n_split = group_end;
   if (parts < 2 || n_split <= 0) return p;
+  p.head_major = 0;  // a split plan claims units in (b, h, t) order
   p.split_from = group_end - n_split;
   p.split_count = n_split;
   p.split_parts = parts;
@@ -139,9 +158,18 @@ CA_HD int64_t slot_to_work(int64_t slot, int64_t n, int64_t n_first, int n_xcd) 
   return n_first + (s0 - f0) + (local - fx);
 }
 
-// The work index of launch slot `slot` under plan p.
+// The work index of launch slot `slot` under plan p.  A head-major plan
+// places position o = (h * n_batch + b) * n_qtiles + t of its order at work
+// index (b * heads + h) * n_qtiles + t.
 CA_HD int64_t plan_slot_work(const Plan& p, int64_t slot) {
-  return slot_to_work(slot, p.n_items, p.n_items_pred, p.n_xcd);
+  const int64_t o = slot_to_work(slot, p.n_items, p.n_items_pred, p.n_xcd);
+  if (!p.head_major) return o;
+  const uint32_t nq = (uint32_t)p.n_qtiles;
+  const uint32_t per_head = (uint32_t)p.n_batch * nq;
+  const uint32_t h = (uint32_t)o / per_head;
+  const uint32_t bt = (uint32_t)o - h * per_head;  // b * n_qtiles + t
+  const uint32_t b = bt / nq;
+  return ((int64_t)b * p.heads + h) * nq + (bt - b * nq);
 }
 
 // Persistent launch: each die x owns the work of its launch slots

@@ -332,7 +332,11 @@ int chunkattn_validate_noise_init(const void *pool, int pool_frames, long long f
  *   q, out  [batch][lq][heads][head_dim]
  *   k, v    batch item b at element offset b * kv_batch_stride, each
  *           [lkv][heads][head_dim]; kv_batch_stride = 0 shares one K/V
- *           (e.g. one prompt's text tokens) across the batch.
+ *           (e.g. one prompt's text tokens) across the batch.  A shared K/V
+ *           runs the work items head by head (all batch items of a head
+ *           together, so that each die's L2 holds few heads' K/V); the
+ *           order changes no result, since every output row is computed by
+ *           one work item.
  *   batch, lq >= 0 (either 0: returns OK); lkv >= 1; kv_batch_stride >= 0.
  *   Other arguments as for chunkattn_queue_step.
  */

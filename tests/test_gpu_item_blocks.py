@@ -13,7 +13,9 @@ tile, ragged last query block inside a multi-block item), cross-attention of
 per-chunk queries over 512 shared text rows (DualParal write-up, section 三:
 cross-attention per chunk, without the cache), a single key tile per block,
 and blocks that leave fp32's range at several positions of an item (the
-recheck pass must find every marked block).
+recheck pass must find every marked block).  A shared K/V runs its items
+head-major; that order must give the same bits as the same K/V copied per
+batch item, in every kernel.
 """
 import sys
 
@@ -149,3 +151,55 @@ def test_overflowing_blocks_inside_items(hot):
     assert torch.isfinite(out).all()
     assert torch.equal(out, ref_out), "multi-block items differ from one-block items"
     assert_parity(to_f64(out), oracle.full(q, k, v), f"overflow blocks {hot}")
+
+
+def _shared_vs_replicated(q, kt, vt, ctx, what):
+    """full() over one shared K/V (kv stride 0: items run head-major) against
+    the same K/V copied per batch item (items in (chunk, head, tile) order):
+    every output row is computed by one item with the same arithmetic, so the
+    two must agree bit for bit, and every element must be written."""
+    B = q.shape[0]
+    kr = kt.expand(B, -1, -1, -1).contiguous()
+    vr = vt.expand(B, -1, -1, -1).contiguous()
+    sent = SENTINEL if q.dtype == torch.bfloat16 else 2.0 ** 120
+    out_s = torch.full_like(q, sent)
+    out_r = torch.full_like(q, sent)
+    ca.full(q, kt, vt, out=out_s, ctx=ctx)
+    ca.full(q, kr, vr, out=out_r, ctx=ctx)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out_s).all() and (out_s.float().abs() < sent / 2).all(), \
+        f"{what}: output not fully written"
+    assert torch.equal(out_s, out_r), f"{what}: shared K/V differs from replicated K/V"
+    return out_s
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_shared_kv_head_major_equals_replicated(G):
+    """16 chunks x 2000 queries, 8 heads, over 512 shared text rows: 768
+    one-block items (several per workgroup, claims across dies) or 256 items of
+    up to 4 blocks; two chunks also against the fp64 oracle."""
+    B, lq, T, H, D = 16, 2000, 512, 8, 128
+    say("case shared kv head-major", G, (B, lq, T, H, D))
+    q = synth.cross_queries(B, lq, H, D, 514, DEV, torch.bfloat16)
+    kt, vt = synth.text_inputs(T, H, D, 514, DEV, torch.bfloat16)
+    out = _shared_vs_replicated(q, kt, vt, ctx_blocks(G), f"G={G}")
+    sel = [0, B - 1]
+    assert_parity(to_f64(out[sel]), oracle.full(q[sel], kt, vt), f"shared kv G={G}")
+
+
+@pytest.mark.parametrize("flags,dtype", [(ca.FLAG_BLOCK256, torch.bfloat16),
+                                         (ca.FLAG_BLOCK128, torch.bfloat16),
+                                         (0, torch.float32)],
+                         ids=["bm256", "bm128", "fp32"])
+def test_shared_kv_head_major_other_kernels(flags, dtype):
+    """The 256- and 128-row kernels and the fp32 kernel take the same
+    head-major order for a shared K/V: 6 items x 1000 queries, 5 heads, 300
+    text rows (ragged last key tile)."""
+    B, lq, T, H, D = 6, 1000, 300, 5, 128
+    say("case shared kv head-major", flags, dtype, (B, lq, T, H, D))
+    q = synth.normal((B, lq, H, D), 515, synth.Q_ID, DEV, dtype)
+    kt = synth.normal((1, T, H, D), 515, synth.K_ID, DEV, dtype)
+    vt = synth.normal((1, T, H, D), 515, synth.V_ID, DEV, dtype)
+    ctx = ca.Context(0, flags)
+    ctx.set_tail_split(0)
+    _shared_vs_replicated(q, kt, vt, ctx, f"flags {flags} {dtype}")

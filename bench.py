@@ -49,6 +49,27 @@ def kernel_name(block_rows: int, D: int, dtype: str) -> str:
     return f"chunk_attn_fwd<{D},{dtype},{block_rows // 32}>"
 
 
+def measure_mfma_peak(ca, ctx, synth, dev, stream, launches: int = 10) -> float:
+    """Dense bf16 rate the device sustains (TFLOP/s): the library's matrix-core
+    probe (one workgroup of 8 waves per CU, back-to-back 16x16x32 bf16 MFMAs,
+    about 4 ms per launch), one warmup launch, then the mean of `launches`
+    launches timed with HIP events on the launch stream.  Run after the timed
+    region, so its heat does not reach the measurement it is set beside."""
+    import torch
+    ops = synth.probe_operands(0, device=dev)
+    out = torch.empty(ctx.cu_count * ca.PROBE_OUT_PER_WORKGROUP, dtype=torch.float32, device=dev)
+    iters = 1 << 15
+    ca.mfma_probe(ops, iters, out, ctx=ctx, stream=stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    flops = 0.0
+    for _ in range(launches):
+        flops += ca.mfma_probe(ops, iters, out, ctx=ctx, stream=stream)[1]
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    return flops / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -69,6 +90,8 @@ def parse():
                          "(queue workloads; 0: unit-scale inputs)")
     ap.add_argument("--exact-scale", action="store_true",
                     help="context with the exact-scale flag (scores scaled in fp32)")
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip the matrix-core rate probe after the timed region")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (counter calibration)")
     ap.add_argument("--linearity", action="store_true",
@@ -234,6 +257,10 @@ def main():
         entry = tr.get(name)
         if entry and entry.get("kernel_hash") == kernel_hash():
             roofline["traffic"] = entry["bytes_per_launch"]
+    if not args.no_mfma_probe:
+        peak = measure_mfma_peak(ca, ctx, synth, dev, stream)
+        roofline["measured_peak"] = round(peak, 1)
+        roofline["frac_of_measured_peak"] = round(achieved / peak, 4)
 
     if args.copy_calibration:
         n_bytes = 1 << 30

@@ -114,6 +114,11 @@ def load_library():
     lib.chunkattn_validate_noise_init.argtypes = [vp, i32, i64, vp, vp, i32, i32, i32, vp, vp]
     lib.chunkattn_ctx_xcd_count.restype = i32
     lib.chunkattn_ctx_xcd_count.argtypes = [vp]
+    lib.chunkattn_ctx_cu_count.restype = i32
+    lib.chunkattn_ctx_cu_count.argtypes = [vp]
+    lib.chunkattn_mfma_probe.restype = i32
+    lib.chunkattn_mfma_probe.argtypes = [vp, vp, i64, vp, ctypes.POINTER(i32),
+                                         ctypes.POINTER(ctypes.c_double), vp]
     _lib = lib
     return lib
 
@@ -161,6 +166,10 @@ class Context:
     @property
     def xcd_count(self) -> int:
         return int(load_library().chunkattn_ctx_xcd_count(self.handle))
+
+    @property
+    def cu_count(self) -> int:
+        return int(load_library().chunkattn_ctx_cu_count(self.handle))
 
     @property
     def block_rows(self) -> int:
@@ -513,6 +522,33 @@ def plan_device(chunk_len: int, n_chunks: int, heads: int, device: int = 0, ctx=
                                      ctypes.c_void_p(items.data_ptr()), n.value,
                                      _stream(items, None)), ctx.handle)
     return items[: n.value]
+
+
+# floats the matrix-core probe writes per workgroup (8 waves x 8 accumulators
+# x 64 lanes x 4)
+PROBE_OUT_PER_WORKGROUP = 8 * 8 * 64 * 4
+PROBE_WORDS = 64 * 32
+
+
+def mfma_probe(operands, iters: int, out, ctx=None, stream=None):
+    """Matrix-core rate probe (chunkattn_mfma_probe): operands is an int32
+    device tensor of 64 x 32 words (bf16 pairs), out a float32 device tensor of
+    at least ctx.cu_count * PROBE_OUT_PER_WORKGROUP elements.  Enqueues one
+    launch; returns (workgroups, FLOPs of the launch)."""
+    lib = load_library()
+    ctx = ctx or create(operands.device.index or 0)
+    if operands.numel() != PROBE_WORDS or operands.element_size() != 4:
+        raise ValueError(f"chunkattn: operands must hold {PROBE_WORDS} 32-bit words")
+    if out.dtype.itemsize != 4 or out.numel() < ctx.cu_count * PROBE_OUT_PER_WORKGROUP:
+        raise ValueError("chunkattn: out must hold cu_count * PROBE_OUT_PER_WORKGROUP floats")
+    for name, t in (("operands", operands), ("out", out)):
+        _require(t, name, operands.device)
+    n_wg = ctypes.c_int()
+    flops = ctypes.c_double()
+    _check(lib.chunkattn_mfma_probe(ctx.handle, ctypes.c_void_p(operands.data_ptr()), iters,
+                                    ctypes.c_void_p(out.data_ptr()), ctypes.byref(n_wg),
+                                    ctypes.byref(flops), _stream(out, stream)), ctx.handle)
+    return n_wg.value, flops.value
 
 
 def validate_queue_step(q_ptr, k_ptr, v_ptr, cache_ptr, out_ptr, chunk_len, n_chunks, heads,

@@ -18,6 +18,7 @@
 #include "attn_wide.h"
 #include "chunkattn.h"
 #include "fifo.h"
+#include "mfma_probe.h"
 #include "noise.h"
 
 // Work-queue slots of a context.  A slot is kQueueWords 64-bit words (one
@@ -1134,6 +1135,35 @@ int chunkattn_noise_init(chunkattn_ctx* ctx, const void* pool, int pool_frames,
   ctx->err.clear();
   return CHUNKATTN_OK;
 }
+
+int chunkattn_mfma_probe(chunkattn_ctx* ctx, const void* operands, long long iters, void* out,
+                         int* n_workgroups_out, double* flops_out, void* hip_stream) {
+  if (!ctx) return set_err(&g_thread_err, CHUNKATTN_EINVAL, "ctx must be non-NULL");
+  if (!operands || !out || ((uintptr_t)operands & 15) || ((uintptr_t)out & 15))
+    return set_err(&ctx->err, CHUNKATTN_EINVAL,
+                   "operands and out must be non-NULL and 16-byte aligned");
+  if (iters < 1 || iters > (1ll << 19))
+    return set_err(&ctx->err, CHUNKATTN_EINVAL, "iters %lld outside [1, 2^19]", iters);
+  DeviceGuard g(ctx->device);
+  if (!g.ok) return set_err(&ctx->err, CHUNKATTN_EDEVICE, "cannot make device current");
+  const int n_wg = ctx->n_cu;
+  hipLaunchKernelGGL(chunkattn::mfma_peak_probe, dim3((unsigned)n_wg),
+                     dim3(chunkattn::kProbeWaves * 64), 0, static_cast<hipStream_t>(hip_stream),
+                     static_cast<const uint32_t*>(operands), iters, static_cast<float*>(out));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return set_err(&ctx->err, CHUNKATTN_ELAUNCH, "mfma_peak_probe launch failed: %s",
+                   hipGetErrorString(e));
+  if (n_workgroups_out) *n_workgroups_out = n_wg;
+  // 16 x 16 x 32 multiply-adds per instruction, 2 FLOPs each
+  if (flops_out)
+    *flops_out = (double)n_wg * chunkattn::kProbeWaves * chunkattn::kProbeAcc * (double)iters *
+                 (2.0 * 16 * 16 * 32);
+  ctx->err.clear();
+  return CHUNKATTN_OK;
+}
+
+int chunkattn_ctx_cu_count(const chunkattn_ctx* ctx) { return ctx ? ctx->n_cu : 0; }
 
 const char* chunkattn_status_string(int status) {
   switch (status) {

@@ -101,3 +101,18 @@ def text_inputs(n_text, H, D, seed: int, device="cpu", dtype=torch.bfloat16):
 def cross_queries(n, L, H, D, seed: int, device="cpu", dtype=torch.bfloat16):
     """Per-chunk cross-attention queries [n][L][H][D]."""
     return normal((n, L, H, D), seed, QX_ID, device, dtype)
+
+
+PROBE_ID = 7
+
+
+def probe_operands(seed: int, device="cpu") -> torch.Tensor:
+    """Operands of the matrix-core rate probe: 64 lanes x 32 words, each word a
+    pair of bf16 values drawn uniformly from {-1, 0, 1} (low half first), as
+    int32.  Small integers keep every product and sum of the probe exact."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed * 1000 + PROBE_ID)
+    vals = torch.randint(-1, 2, (64, 64), generator=g).to(torch.float32)
+    bits = vals.to(torch.bfloat16).view(torch.int16).to(torch.int32) & 0xFFFF
+    words = bits[:, 0::2] | (bits[:, 1::2] << 16)
+    return words.to(torch.int32).contiguous().to(device)

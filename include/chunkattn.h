@@ -410,6 +410,37 @@ int chunkattn_plan_device(chunkattn_ctx *ctx, int chunk_len, int n_chunks, int h
 /* Number of accelerator dies (XCDs) the context uses for its launch order. */
 int chunkattn_ctx_xcd_count(const chunkattn_ctx *ctx);
 
+/*
+ * Matrix-core rate probe, a measurement aid beside the attention path (it
+ * computes nothing of the method): the dense bf16 rate the device sustains
+ * under its own clock and power limit, against which the attention kernels'
+ * throughput can be stated besides the rate quoted at 2.4 GHz.  One launch on
+ * hip_stream: one workgroup of 8 waves per CU; every wave loads four operand
+ * pairs (A, B) of the 16x16x32 bf16 matrix instruction and runs `iters`
+ * rounds of 8 independent such instructions (accumulator a adds A_{a%4} B_{a%4}).
+ *
+ *   operands  device, 64 lanes x 32 words (pairs of bf16): lane l's words
+ *             8s..8s+3 are its A fragment of pair s (row l % 16 of A, columns
+ *             8*(l/16) .. +7), words 8s+4..8s+7 its B fragment (column l % 16
+ *             of B, rows 8*(l/16) .. +7); the same for every wave.
+ *   iters     rounds, 1 .. 2^19 (so that with entries in {-1, 0, 1} every
+ *             accumulator stays an exact integer in fp32).
+ *   out       device, n_workgroups * 8 waves * 8 accumulators * 64 lanes * 4
+ *             floats: lane l's 4 values of accumulator a are rows
+ *             4*(l/16) .. +3, column l % 16, of iters * A_{a%4} B_{a%4}.
+ *   n_workgroups_out  receives the launch's workgroup count (the context's CU
+ *             count), so out must hold chunkattn_ctx_cu_count(ctx) * 16384
+ *             floats.
+ *   flops_out receives the launch's FLOP count (2 per multiply-add).
+ * Errors: CHUNKATTN_EINVAL for NULL or unaligned pointers or iters out of
+ * range, CHUNKATTN_ELAUNCH if the launch fails.
+ */
+int chunkattn_mfma_probe(chunkattn_ctx *ctx, const void *operands, long long iters, void *out,
+                         int *n_workgroups_out, double *flops_out, void *hip_stream);
+
+/* Number of compute units of the context's device. */
+int chunkattn_ctx_cu_count(const chunkattn_ctx *ctx);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,14 +52,16 @@ def kernel_name(block_rows: int, D: int, dtype: str) -> str:
 def measure_mfma_peak(ca, ctx, synth, dev, stream, launches: int = 10) -> float:
     """Dense bf16 rate the device sustains (TFLOP/s): the library's matrix-core
     probe (one workgroup of 8 waves per CU, back-to-back 16x16x32 bf16 MFMAs,
-    about 4 ms per launch), one warmup launch, then the mean of `launches`
+    about 4 ms per launch), `launches` warmup launches (the clock climbs for
+    about 30 ms after the attention pass), then the mean of `launches`
     launches timed with HIP events on the launch stream.  Run after the timed
     region, so its heat does not reach the measurement it is set beside."""
     import torch
     ops = synth.probe_operands(0, device=dev)
     out = torch.empty(ctx.cu_count * ca.PROBE_OUT_PER_WORKGROUP, dtype=torch.float32, device=dev)
     iters = 1 << 15
-    ca.mfma_probe(ops, iters, out, ctx=ctx, stream=stream)
+    for _ in range(launches):
+        ca.mfma_probe(ops, iters, out, ctx=ctx, stream=stream)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
     flops = 0.0

@@ -245,6 +245,7 @@ def main():
         "kernel": kernel_name(ctx.call_block_rows(w.D, ca.BF16 if w.dtype == "bf16" else ca.F32),
                               w.D, w.dtype),
         "launch_ms_avg": round(dom_avg_ms, 4),
+        "launch_ms_median": round(float(np.median(launch_ms)), 4),
         "launch_ms_min": round(float(launch_ms.min()), 4),
         "launch_ms_p90": round(float(np.percentile(launch_ms, 90)), 4),
     }

@@ -94,6 +94,9 @@ def parse():
                     help="context with the exact-scale flag (scores scaled in fp32)")
     ap.add_argument("--no-mfma-probe", action="store_true",
                     help="skip the matrix-core rate probe after the timed region")
+    ap.add_argument("--mfma-probe-only", action="store_true",
+                    help="instead of the attention step: the matrix-core probe alone, "
+                         "--warmup untimed and --steps timed launches (about 4 ms each)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain device copy of known size (counter calibration)")
     ap.add_argument("--linearity", action="store_true",
@@ -118,6 +121,9 @@ def main():
 
     if args.linearity:
         bench_linearity(args)
+        return
+    if args.mfma_probe_only:
+        bench_mfma_probe(args)
         return
     name = args.workload or configs.BENCH_WORKLOAD
     if name in configs.NOISE_WORKLOADS:
@@ -330,6 +336,56 @@ def main():
         else:
             record["cpu_baseline"] = cpu_baseline(w, q, k, v, cache, args.cpu_seconds)
 
+    print(json.dumps(record), flush=True)
+
+
+def bench_mfma_probe(args):
+    """The library's matrix-core probe alone: the dense bf16 rate this device
+    sustains on back-to-back MFMAs (one JSON line)."""
+    import numpy as np
+    import torch
+
+    from chunked_spatio_temporal_amd import chunkattn as ca
+    from chunked_spatio_temporal_amd import synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    ca.load_library()
+    ctx = ca.create(0)
+    stream = torch.cuda.current_stream(dev)
+    ops = synth.probe_operands(0, device=dev)
+    out = torch.empty(ctx.cu_count * ca.PROBE_OUT_PER_WORKGROUP, dtype=torch.float32, device=dev)
+    iters = 1 << 15
+    for _ in range(args.warmup):
+        ca.mfma_probe(ops, iters, out, ctx=ctx, stream=stream)
+    steps = max(args.steps, 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    flops = 0.0
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        flops = ca.mfma_probe(ops, iters, out, ctx=ctx, stream=stream)[1]
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    rate = flops / (float(ms.mean()) * 1e-3) / 1e12
+    record = {
+        "metric": "dense bf16 MFMA rate sustained by the matrix-core probe",
+        "value": round(rate, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(float(ms.mean()), 4),
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "mfma_probe", "workgroups": ctx.cu_count, "waves_per_workgroup": 8,
+                   "instruction": "v_mfma_f32_16x16x32_bf16", "rounds_per_launch": iters,
+                   "flops_per_launch": flops},
+        "roofline": {"bound": "mfma", "achieved": round(rate, 2),
+                     "peak": round(BF16_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(rate / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "mfma_peak_probe",
+                     "launch_ms_min": round(float(ms.min()), 4),
+                     "launch_ms_max": round(float(ms.max()), 4)},
+        "cpu_baseline": None,
+    }
     print(json.dumps(record), flush=True)
 
 

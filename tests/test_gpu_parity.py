@@ -88,6 +88,11 @@ SHAPES = [
     (2, 333, 1, 64, torch.float32),
     (5, 129, 2, 128, torch.bfloat16),
     (1, 300, 3, 128, torch.bfloat16),
+    # 384-row item boundaries: a 1-row last item, a full 256-row last item
+    # (two query blocks per wave), whole 384-row items only
+    (2, 385, 2, 128, torch.bfloat16),
+    (2, 640, 1, 128, torch.bfloat16),
+    (3, 768, 1, 128, torch.bfloat16),
 ]
 
 
